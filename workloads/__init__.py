@@ -1,0 +1,320 @@
+"""Seeded synthetic inputs for the dense GEMM workloads.
+
+This module is shared by the CPU oracle side (tests, cpu baseline) and the
+GPU side (tests, bench).  It holds no GEMM arithmetic: it only draws random
+numbers, converts them to the storage dtype with a library cast (torch's CPU
+fp32 -> bfloat16 cast, round-to-nearest-even) and lays the logical matrices
+out in memory with the requested order, leading dimension and batch stride.
+
+The problem statement is the one of "La GEMM, de zero a cuBLAS" section 2.1
+(C = alpha*A*B + beta*C) together with the inputs listed in "Skill: Write a
+Triton GEMM Kernel", section "Inputs the agent should gather first" (sizes,
+dtype, per-operand layout, output dtype, epilogue, batch/broadcast).
+
+Seeds: operand ``o`` of workload ``w`` is drawn from
+``numpy.random.default_rng([w, o])`` with o = 0 (A), 1 (B), 2 (C_in), 3 (bias).
+Uniform U(a, b) is drawn in fp64 and cast to fp32; normal N(0, s) is
+``standard_normal * s`` cast to fp32 (s is the standard deviation).  bf16
+operands are the RNE rounding of those fp32 values.  The "small integer twin"
+of a workload draws every operand from {-2, ..., 2} instead.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+F32 = "f32"
+BF16 = "bf16"
+ROW = "row"
+COL = "col"
+
+ACT_NONE = "none"
+ACT_GELU_ERF = "gelu_erf"
+ACT_GELU_TANH = "gelu_tanh"
+
+_ELEM_BYTES = {F32: 4, BF16: 2}
+
+
+@dataclasses.dataclass(frozen=True)
+class Problem:
+    """One GEMM problem: shapes, dtypes, layouts and epilogue.
+
+    Layout conventions (element units):
+      A is M x K, B is K x N, C is M x N, each ``batch`` times.
+      Row-major X with leading dimension ld stores X[r][c] at r*ld + c;
+      column-major stores it at c*ld + r.  Matrix b of a batch starts at
+      b*stride.  A or B with stride 0 is broadcast to every batch entry.
+    """
+    name: str
+    M: int
+    N: int
+    K: int
+    batch: int = 1
+    a_type: str = F32
+    b_type: str = F32
+    c_type: str = F32
+    a_order: str = ROW
+    b_order: str = ROW
+    c_order: str = ROW
+    lda: Optional[int] = None
+    ldb: Optional[int] = None
+    ldc: Optional[int] = None
+    stride_a: Optional[int] = None
+    stride_b: Optional[int] = None
+    stride_c: Optional[int] = None
+    alpha: float = 1.0
+    beta: float = 0.0
+    has_bias: bool = False
+    bias_type: str = F32
+    act: str = ACT_NONE
+    split_k: int = 0
+    # distributions: ("uniform", lo, hi) or ("normal", std)
+    dist_a: tuple = ("uniform", -1.0, 1.0)
+    dist_b: tuple = ("uniform", -1.0, 1.0)
+    dist_c: tuple = ("uniform", -1.0, 1.0)
+    dist_bias: tuple = ("uniform", -0.5, 0.5)
+    seed: int = 0
+
+    # --- derived layout -------------------------------------------------
+    def _ld(self, order, rows, cols, given):
+        if given is not None:
+            return int(given)
+        return max(1, cols if order == ROW else rows)
+
+    @property
+    def lda_(self):
+        return self._ld(self.a_order, self.M, self.K, self.lda)
+
+    @property
+    def ldb_(self):
+        return self._ld(self.b_order, self.K, self.N, self.ldb)
+
+    @property
+    def ldc_(self):
+        return self._ld(self.c_order, self.M, self.N, self.ldc)
+
+    @staticmethod
+    def _span(order, rows, cols, ld):
+        if rows == 0 or cols == 0:
+            return 0
+        if order == ROW:
+            return (rows - 1) * ld + cols
+        return (cols - 1) * ld + rows
+
+    def _stride(self, given, span):
+        return int(given) if given is not None else span
+
+    @property
+    def stride_a_(self):
+        return self._stride(self.stride_a, self._span(self.a_order, self.M, self.K, self.lda_))
+
+    @property
+    def stride_b_(self):
+        return self._stride(self.stride_b, self._span(self.b_order, self.K, self.N, self.ldb_))
+
+    @property
+    def stride_c_(self):
+        return self._stride(self.stride_c, self._span(self.c_order, self.M, self.N, self.ldc_))
+
+    def buffer_elems(self, which):
+        """Number of elements the storage buffer of operand 'a'|'b'|'c' spans."""
+        if which == "a":
+            span = self._span(self.a_order, self.M, self.K, self.lda_)
+            stride = self.stride_a_
+        elif which == "b":
+            span = self._span(self.b_order, self.K, self.N, self.ldb_)
+            stride = self.stride_b_
+        else:
+            span = self._span(self.c_order, self.M, self.N, self.ldc_)
+            stride = self.stride_c_
+        if self.batch == 0 or span == 0:
+            return 0
+        return (self.batch - 1) * stride + span
+
+    def flops(self):
+        return 2.0 * self.batch * self.M * self.N * self.K
+
+    def replace(self, **kw):
+        return dataclasses.replace(self, **kw)
+
+
+def elem_bytes(dtype):
+    return _ELEM_BYTES[dtype]
+
+
+# ---------------------------------------------------------------------------
+# The five workloads.  Layout readings where the statement is silent:
+# C4 and C5 use the C3 layout (A row-major, B column-major, C row-major),
+# alpha = 1, beta = 0; N(0, 0.5) means standard deviation 0.5; the C4 bias
+# is bf16.
+# ---------------------------------------------------------------------------
+WORKLOADS = {
+    "c1": Problem(
+        name="sgemm_f32_256", M=256, N=256, K=256,
+        a_type=F32, b_type=F32, c_type=F32,
+        alpha=1.5, beta=0.5,
+        dist_a=("uniform", -1.0, 1.0), dist_b=("uniform", -1.0, 1.0),
+        dist_c=("uniform", -1.0, 1.0), seed=1),
+    "c2": Problem(
+        name="sgemm_f32_4096", M=4096, N=4096, K=4096,
+        a_type=F32, b_type=F32, c_type=F32,
+        alpha=1.0, beta=0.0,
+        dist_a=("uniform", -1.0, 1.0), dist_b=("uniform", -1.0, 1.0), seed=2),
+    "c3": Problem(
+        name="gemm_bf16_4096", M=4096, N=4096, K=4096,
+        a_type=BF16, b_type=BF16, c_type=BF16,
+        a_order=ROW, b_order=COL, c_order=ROW,
+        alpha=1.0, beta=0.0,
+        dist_a=("normal", 1.0), dist_b=("normal", 1.0), seed=3),
+    "c4": Problem(
+        name="gemm_bf16_4095x4097x1000_bias_gelu", M=4095, N=4097, K=1000,
+        a_type=BF16, b_type=BF16, c_type=BF16,
+        a_order=ROW, b_order=COL, c_order=ROW,
+        alpha=1.0, beta=0.0, has_bias=True, bias_type=BF16, act=ACT_GELU_ERF,
+        dist_a=("normal", 0.5), dist_b=("normal", 0.5),
+        dist_bias=("uniform", -0.5, 0.5), seed=4),
+    "c5": Problem(
+        name="gemm_bf16_batch32_128x128x16384_splitk", M=128, N=128, K=16384,
+        batch=32,
+        a_type=BF16, b_type=BF16, c_type=F32,
+        a_order=ROW, b_order=COL, c_order=ROW,
+        stride_b=0,
+        alpha=1.0, beta=0.0,
+        dist_a=("normal", 1.0), dist_b=("normal", 1.0), seed=5),
+}
+
+
+# ---------------------------------------------------------------------------
+# Drawing values
+# ---------------------------------------------------------------------------
+def _draw(rng, dist, n, small_int):
+    if small_int:
+        return rng.integers(-2, 3, size=n).astype(np.float32)
+    kind = dist[0]
+    if kind == "uniform":
+        return rng.uniform(dist[1], dist[2], size=n).astype(np.float32)
+    if kind == "normal":
+        return (rng.standard_normal(size=n) * dist[1]).astype(np.float32)
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def to_storage(values_f32, dtype):
+    """fp32 values -> storage array (float32, or uint16 bf16 bit patterns).
+
+    bf16 uses torch's CPU cast (round to nearest, ties to even)."""
+    values_f32 = np.ascontiguousarray(values_f32, dtype=np.float32)
+    if dtype == F32:
+        return values_f32
+    import torch
+    t = torch.from_numpy(values_f32).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def storage_dtype(dtype):
+    return np.float32 if dtype == F32 else np.uint16
+
+
+def _fill_value(dtype, fill):
+    if fill is None:
+        return 0
+    if dtype == F32:
+        return np.float32(fill)
+    # bf16 sentinels as bit patterns
+    if isinstance(fill, float) and np.isnan(fill):
+        return np.uint16(0x7FC1)
+    return to_storage(np.array([fill], np.float32), BF16)[0]
+
+
+def lay_out(logical, order, ld, stride, n_elems, dtype, fill=None):
+    """Place logical matrices [batch][rows][cols] (storage dtype) into a flat
+    buffer with the given order / ld / batch stride.  Positions not covered
+    by any matrix element hold ``fill`` (0 unless given: NaN sentinels let
+    tests see stray reads)."""
+    buf = np.full(n_elems, _fill_value(dtype, fill), dtype=storage_dtype(dtype))
+    batch, rows, cols = logical.shape
+    r = np.arange(rows)[:, None]
+    c = np.arange(cols)[None, :]
+    off = (r * ld + c) if order == ROW else (c * ld + r)
+    for b in range(batch):
+        buf[b * stride + off] = logical[b]
+        if stride == 0:
+            break
+    return buf
+
+
+def read_back(buf, order, ld, stride, batch, rows, cols):
+    """Inverse of lay_out: gather logical [batch][rows][cols] from a buffer."""
+    r = np.arange(rows)[:, None]
+    c = np.arange(cols)[None, :]
+    off = (r * ld + c) if order == ROW else (c * ld + r)
+    out = np.empty((batch, rows, cols), dtype=buf.dtype)
+    for b in range(batch):
+        out[b] = buf[b * stride + off]
+    return out
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Host buffers of one problem instance (storage dtype, flat)."""
+    problem: Problem
+    A: np.ndarray
+    B: np.ndarray
+    C: np.ndarray          # C_in (also the output buffer's initial content)
+    bias: Optional[np.ndarray]
+    # logical operands (storage dtype) for tests that index them directly
+    A_log: np.ndarray
+    B_log: np.ndarray
+    C_log: np.ndarray
+
+
+def make_inputs(p: Problem, small_int=False, fill=None, c_fill=None, seed=None):
+    """Draw the operands of ``p`` and lay them out.
+
+    ``fill`` is written to every position of the A/B/C buffers that no
+    matrix element covers (padding beyond the extent, gaps between batch
+    entries).  ``c_fill`` (if given) replaces the drawn C_in values."""
+    seed = p.seed if seed is None else seed
+    a_batches = 1 if p.stride_a_ == 0 else p.batch
+    b_batches = 1 if p.stride_b_ == 0 else p.batch
+    rng = np.random.default_rng([seed, 0])
+    A_log = to_storage(_draw(rng, p.dist_a, a_batches * p.M * p.K, small_int), p.a_type)
+    A_log = A_log.reshape(a_batches, p.M, p.K)
+    rng = np.random.default_rng([seed, 1])
+    B_log = to_storage(_draw(rng, p.dist_b, b_batches * p.K * p.N, small_int), p.b_type)
+    B_log = B_log.reshape(b_batches, p.K, p.N)
+    rng = np.random.default_rng([seed, 2])
+    if c_fill is None:
+        C_log = to_storage(_draw(rng, p.dist_c, p.batch * p.M * p.N, small_int), p.c_type)
+    else:
+        C_log = np.full(p.batch * p.M * p.N, _fill_value(p.c_type, c_fill),
+                        dtype=storage_dtype(p.c_type))
+    C_log = C_log.reshape(p.batch, p.M, p.N)
+    bias = None
+    if p.has_bias:
+        rng = np.random.default_rng([seed, 3])
+        bias = to_storage(_draw(rng, p.dist_bias, p.N, small_int), p.bias_type)
+    A = lay_out(A_log, p.a_order, p.lda_, p.stride_a_, p.buffer_elems("a"), p.a_type, fill)
+    B = lay_out(B_log, p.b_order, p.ldb_, p.stride_b_, p.buffer_elems("b"), p.b_type, fill)
+    C = lay_out(C_log, p.c_order, p.ldc_, p.stride_c_, p.buffer_elems("c"), p.c_type, fill)
+    return Inputs(p, A, B, C, bias, A_log, B_log, C_log)
+
+
+def sample_points(p: Problem, n, seed=12345):
+    """Seeded output coordinates (b, i, j) for sampled parity checks at full
+    size.  Always includes the four corners of the first and last batch entry
+    so ragged edges are covered."""
+    rng = np.random.default_rng([seed, p.M, p.N, p.K, p.batch])
+    b = rng.integers(0, max(p.batch, 1), size=n)
+    i = rng.integers(0, max(p.M, 1), size=n)
+    j = rng.integers(0, max(p.N, 1), size=n)
+    corners = []
+    for bb in {0, p.batch - 1}:
+        for ii in {0, p.M - 1}:
+            for jj in {0, p.N - 1}:
+                corners.append((bb, ii, jj))
+    cb, ci, cj = (np.array(x, dtype=np.int64) for x in zip(*corners))
+    return (np.concatenate([cb, b]).astype(np.int64),
+            np.concatenate([ci, i]).astype(np.int64),
+            np.concatenate([cj, j]).astype(np.int64))
