@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the dense GEMM library on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5]
+
+A step is one call of the library (dg_gemm through the C ABI) on one
+workload whose operands are already resident in HBM: scheduler, loader,
+inner loop, epilogue (and split-K reduction when planned) all run inside the
+timed region.  Timing uses HIP events recorded on the stream the kernels are
+launched on, after W untimed warm-up steps, bracketed by device
+synchronisation.  Throughput is TFLOPS = 2MNK / t ("GEMM Kernel
+Optimization", Verification).
+
+The default workload is the fp32 SGEMM at M = N = K = 4096; the bf16 GEMM at
+4096^3 (the other half of the headline metric) is measured in the same run
+and reported under "secondary".  The CPU oracle is timed on a bounded,
+seeded sample of the same workload's output elements on this host's cores.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TFLOPS=2MNK/t at 4096³ bf16 & fp32, as % of MI355X MFMA/FP32 peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _dtype_name(p):
+    return "f32" if p.a_type == "f32" else "bf16"
+
+
+def _roofline_peak(p, kernel):
+    """(bound, peak FLOP/s) of the workload's dominant kernel."""
+    from dense_gemm_10_amd import accounting as acc
+    if kernel == "valu_f32":
+        return "alu", acc.PEAK_F32_VALU_UNPACKED
+    if kernel.startswith("mfma_bf16"):
+        t_c = acc.problem_flops(p) / acc.PEAK_BF16_MFMA
+        t_m = acc.problem_bytes(p) / acc.PEAK_HBM
+        if t_m > t_c:
+            return "hbm", acc.PEAK_HBM
+        return "mfma", acc.PEAK_BF16_MFMA
+    if kernel.startswith("mfma_f32"):
+        return "mfma", acc.PEAK_F32
+    return "alu", acc.PEAK_F32_VALU_UNPACKED
+
+
+def time_workload(name, steps, warmup, **desc_overrides):
+    """Run one workload: returns dict with ms/step, TFLOPS, plan string."""
+    import torch
+    import workloads as W
+    from workloads.device import DeviceProblem
+    p = W.WORKLOADS[name]
+    log(f"[bench] {name}: generating {p.name}")
+    x = W.make_inputs(p)
+    dp = DeviceProblem(p, x, **desc_overrides)
+    plan = dp.describe()
+    log(f"[bench] {name}: plan {plan}")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        dp.run(stream.cuda_stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        dp.run(stream.cuda_stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    flops = p.flops()
+    return dict(problem=p, inputs=x, ms=ms, tflops=flops / (ms * 1e-3) / 1e12, plan=plan,
+                kernel=plan.split()[0].split("=")[1])
+
+
+def cpu_baseline(name, budget_s=12.0):
+    """Oracle throughput on a seeded sample of the workload's outputs."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    p = W.WORKLOADS[name]
+    x = W.make_inputs(p)
+    pb, pi, pj = W.sample_points(p, 4_000_000, seed=777)
+    done, chunk, t0 = 0, 2048, time.perf_counter()
+    while done < pb.size:
+        sl = slice(done, min(done + chunk, pb.size))
+        oracle.gemm_points(p, x.A, x.B, x.C, x.bias, pb[sl], pi[sl], pj[sl])
+        done = sl.stop
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+        chunk = min(chunk * 2, 262144)
+    el = time.perf_counter() - t0
+    flops = 2.0 * p.K * done
+    return {"value": flops / el / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{done} seeded output elements of {p.name} (each a K={p.K} fp64 dot "
+                      f"product plus epilogue), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--secondary", default="c3",
+                    help="second workload reported in the same line ('none' to skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--algo", type=int, default=0)
+    ap.add_argument("--group-m", type=int, default=0)
+    ap.add_argument("--xcd-remap", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import dense_gemm_10_amd as dg
+    from dense_gemm_10_amd import accounting as acc
+
+    overrides = dict(algo=args.algo, group_m=args.group_m, xcd_remap=args.xcd_remap)
+    main_r = time_workload(args.workload, args.steps, args.warmup, **overrides)
+    p = main_r["problem"]
+    bound, peak = _roofline_peak(p, main_r["kernel"])
+    published = acc.compute_peak_for(p)
+    if bound == "hbm":
+        achieved = acc.problem_bytes(p) / (main_r["ms"] * 1e-3)
+        roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": peak / 1e9, "unit": "GB/s",
+                "frac": achieved / peak, "traffic": None}
+    else:
+        achieved = p.flops() / (main_r["ms"] * 1e-3)
+        roof = {"bound": bound, "achieved": achieved / 1e12, "peak": peak / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None}
+    roof["kernel"] = main_r["kernel"]
+    roof["algorithmic_bytes"] = acc.problem_bytes(p)
+    roof["algorithmic_flops"] = p.flops()
+
+    secondary = None
+    if args.secondary != "none" and args.secondary != args.workload:
+        s = time_workload(args.secondary, args.steps, args.warmup, **overrides)
+        sp = s["problem"]
+        sb, spk = _roofline_peak(sp, s["kernel"])
+        secondary = {"workload": sp.name, "value": s["tflops"], "unit": "TFLOPS",
+                     "ms_per_step": s["ms"], "dtype": _dtype_name(sp), "plan": s["plan"],
+                     "frac_of_published_peak": s["tflops"] * 1e12 / acc.compute_peak_for(sp),
+                     "roofline": {"bound": sb, "peak": spk / 1e12 if sb != "hbm" else spk / 1e9,
+                                  "unit": "TFLOP/s" if sb != "hbm" else "GB/s"}}
+        del s
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        cpu = cpu_baseline(args.workload)
+
+    line = {
+        "metric": METRIC,
+        "value": main_r["tflops"],
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_r["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": _dtype_name(p),
+        "data": "synthetic",
+        "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
+                   "a_order": p.a_order, "b_order": p.b_order, "c_type": p.c_type,
+                   "alpha": p.alpha, "beta": p.beta, "act": p.act, "plan": main_r["plan"],
+                   "parallelism": "single_gpu"},
+        "frac_of_published_peak": main_r["tflops"] * 1e12 / published,
+        "published_peak_tflops": published / 1e12,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+        "library_version": dg.dg_version(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

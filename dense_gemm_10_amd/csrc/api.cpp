@@ -1,0 +1,452 @@
+// C ABI of the GEMM library: host-side validation (no HIP calls), plan
+// selection (kernel family, tile, split-K, grid) and launches.
+//
+// Launcher behaviour follows "Skill: Write a Triton GEMM Kernel" (Output
+// format: compute the grid, deal with strides; Common failure modes: the
+// grid uses ceiling division, strides are never recomputed from shapes),
+// the problem statement of "La GEMM, de zero a cuBLAS" section 2.1, and the
+// split-K rule of the Skill page's kernel design rules (split K only when
+// the output tiles alone cannot fill the GPU and K is long; partials go
+// to a workspace and a separate pass reduces them).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/densegemm.h"
+#include "launch.hpp"
+
+using namespace dg;
+
+namespace {
+
+constexpr int64_t kNumCu = 256;          // MI355X compute units
+constexpr int32_t kDefaultGroupM = 8;    // "GEMM Kernel Optimization", L2 Cache Grouping
+constexpr int32_t kMaxSplits = 256;
+
+int64_t elem_size(int32_t t) { return t == DG_BF16 ? 2 : 4; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
+bool add_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_add_overflow(a, b, out); }
+
+// Elements spanned by one rows x cols matrix with the given order and ld.
+bool matrix_span(int32_t order, int64_t rows, int64_t cols, int64_t ld, int64_t *span)
+{
+    if (rows == 0 || cols == 0) {
+        *span = 0;
+        return true;
+    }
+    int64_t outer = order == DG_ROW_MAJOR ? rows : cols;
+    int64_t inner = order == DG_ROW_MAJOR ? cols : rows;
+    int64_t t;
+    return mul_ok(outer - 1, ld, &t) && add_ok(t, inner, span);
+}
+
+// Elements spanned by the whole batch.
+bool batch_span(int64_t span, int64_t batch, int64_t stride, int64_t *total)
+{
+    if (span == 0 || batch == 0) {
+        *total = 0;
+        return true;
+    }
+    int64_t t;
+    return mul_ok(batch - 1, stride, &t) && add_ok(t, span, total);
+}
+
+struct Extents {
+    int64_t a_bytes, b_bytes, c_bytes, bias_bytes;
+    int64_t c_span;
+};
+
+bool ranges_overlap(const void *p, int64_t pn, const void *q, int64_t qn)
+{
+    if (!p || !q || pn <= 0 || qn <= 0)
+        return false;
+    uintptr_t a0 = (uintptr_t)p, a1 = a0 + (uintptr_t)pn;
+    uintptr_t b0 = (uintptr_t)q, b1 = b0 + (uintptr_t)qn;
+    return a0 < b1 && b0 < a1;
+}
+
+bool is_noop(const dg_gemm_desc *d) { return d->M == 0 || d->N == 0 || d->batch == 0; }
+
+bool reads_ab(const dg_gemm_desc *d) { return d->alpha != 0.0f && d->K > 0; }
+
+// Descriptor checks.  No HIP call is made here.
+dg_status validate_desc(const dg_gemm_desc *d, Extents *ext)
+{
+    if (!d || d->struct_size != sizeof(dg_gemm_desc))
+        return DG_ERROR_INVALID_VALUE;
+    if (d->M < 0 || d->N < 0 || d->K < 0 || d->batch < 0)
+        return DG_ERROR_INVALID_VALUE;
+    auto dtype_ok = [](int32_t t) { return t == DG_F32 || t == DG_BF16; };
+    auto order_ok = [](int32_t o) { return o == DG_ROW_MAJOR || o == DG_COL_MAJOR; };
+    if (!dtype_ok(d->a_type) || !dtype_ok(d->b_type) || !dtype_ok(d->c_type))
+        return DG_ERROR_INVALID_VALUE;
+    if (!order_ok(d->a_order) || !order_ok(d->b_order) || !order_ok(d->c_order))
+        return DG_ERROR_INVALID_VALUE;
+    if (d->act < DG_ACT_NONE || d->act > DG_ACT_GELU_TANH)
+        return DG_ERROR_INVALID_VALUE;
+    if (d->algo < DG_ALGO_AUTO || d->algo > DG_ALGO_MFMA_F32)
+        return DG_ERROR_INVALID_VALUE;
+    if (d->split_k < 0 || d->group_m < 0 || d->xcd_remap < -1 || d->xcd_remap > 1)
+        return DG_ERROR_INVALID_VALUE;
+    if (d->bias && !dtype_ok(d->bias_type))
+        return DG_ERROR_INVALID_VALUE;
+    if (d->lda < 1 || d->ldb < 1 || d->ldc < 1)
+        return DG_ERROR_INVALID_VALUE;
+    if (d->stride_a < 0 || d->stride_b < 0 || d->stride_c < 0)
+        return DG_ERROR_INVALID_VALUE;
+    // leading dimension >= length of the contiguous dimension
+    if (d->lda < (d->a_order == DG_ROW_MAJOR ? d->K : d->M))
+        return DG_ERROR_INVALID_VALUE;
+    if (d->ldb < (d->b_order == DG_ROW_MAJOR ? d->N : d->K))
+        return DG_ERROR_INVALID_VALUE;
+    if (d->ldc < (d->c_order == DG_ROW_MAJOR ? d->N : d->M))
+        return DG_ERROR_INVALID_VALUE;
+    // supported dtype combinations
+    if (d->a_type != d->b_type)
+        return DG_ERROR_NOT_SUPPORTED;
+    if (d->a_type == DG_F32 && d->c_type != DG_F32)
+        return DG_ERROR_NOT_SUPPORTED;
+    if (d->split_k > kMaxSplits)
+        return DG_ERROR_NOT_SUPPORTED;
+
+    int64_t sa, sb, sc, ta, tb, tc;
+    if (!matrix_span(d->a_order, d->M, d->K, d->lda, &sa) ||
+        !matrix_span(d->b_order, d->K, d->N, d->ldb, &sb) ||
+        !matrix_span(d->c_order, d->M, d->N, d->ldc, &sc))
+        return DG_ERROR_INVALID_VALUE;
+    if (!batch_span(sa, d->batch, d->stride_a, &ta) || !batch_span(sb, d->batch, d->stride_b, &tb) ||
+        !batch_span(sc, d->batch, d->stride_c, &tc))
+        return DG_ERROR_INVALID_VALUE;
+    // C matrices of different batch entries must not overlap
+    if (d->batch > 1 && sc > 0 && d->stride_c < sc)
+        return DG_ERROR_INVALID_VALUE;
+    int64_t ab, bb, cb;
+    if (!mul_ok(ta, elem_size(d->a_type), &ab) || !mul_ok(tb, elem_size(d->b_type), &bb) ||
+        !mul_ok(tc, elem_size(d->c_type), &cb))
+        return DG_ERROR_INVALID_VALUE;
+    // work size must be addressable
+    int64_t mn, bmn;
+    if (!mul_ok(d->M, d->N, &mn) || !mul_ok(mn, d->batch, &bmn))
+        return DG_ERROR_INVALID_VALUE;
+    if (ext) {
+        ext->a_bytes = ab;
+        ext->b_bytes = bb;
+        ext->c_bytes = cb;
+        ext->bias_bytes = d->bias ? d->N * elem_size(d->bias_type) : 0;
+        ext->c_span = sc;
+    }
+    return DG_SUCCESS;
+}
+
+dg_status validate_ptrs(const dg_gemm_desc *d, const Extents &e, const void *A, const void *B,
+                        const void *C)
+{
+    if (is_noop(d))
+        return DG_SUCCESS;
+    if (!C)
+        return DG_ERROR_INVALID_VALUE;
+    if (reads_ab(d) && (!A || !B))
+        return DG_ERROR_INVALID_VALUE;
+    auto aligned = [](const void *p, int64_t a) { return p == nullptr || ((uintptr_t)p % a) == 0; };
+    if (!aligned(A, elem_size(d->a_type)) || !aligned(B, elem_size(d->b_type)) ||
+        !aligned(C, elem_size(d->c_type)) || (d->bias && !aligned(d->bias, elem_size(d->bias_type))))
+        return DG_ERROR_INVALID_VALUE;
+    if (reads_ab(d) &&
+        (ranges_overlap(C, e.c_bytes, A, e.a_bytes) || ranges_overlap(C, e.c_bytes, B, e.b_bytes)))
+        return DG_ERROR_INVALID_VALUE;
+    if (ranges_overlap(C, e.c_bytes, d->bias, e.bias_bytes))
+        return DG_ERROR_INVALID_VALUE;
+    return DG_SUCCESS;
+}
+
+bool aligned_to(const void *p, int64_t bytes) { return ((uintptr_t)p % bytes) == 0; }
+
+// Eligibility of the specialised kernels.  Pointers may be NULL (query
+// without buffers): they then count as aligned.
+bool valu_eligible(const dg_gemm_desc *d, const void *A, const void *B)
+{
+    if (d->a_type != DG_F32)
+        return false;
+    return aligned_to(A, 16) && aligned_to(B, 16) && d->lda % 4 == 0 && d->ldb % 4 == 0 &&
+           d->stride_a % 4 == 0 && d->stride_b % 4 == 0;
+}
+
+bool mfma_bf16_eligible(const dg_gemm_desc *d, const void *A, const void *B)
+{
+    if (d->a_type != DG_BF16 || d->a_order != DG_ROW_MAJOR || d->b_order != DG_COL_MAJOR)
+        return false;
+    return aligned_to(A, 16) && aligned_to(B, 16) && d->lda % 8 == 0 && d->ldb % 8 == 0 &&
+           d->stride_a % 8 == 0 && d->stride_b % 8 == 0;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t tiles_of(const dg_gemm_desc *d, const TileConfig &t)
+{
+    return ceil_div(d->M, t.bm) * ceil_div(d->N, t.bn) * d->batch;
+}
+
+// Pick the bf16 MFMA tile: the largest tile that keeps at least about
+// half of the compute units busy.
+TileConfig pick_mfma_tile(const dg_gemm_desc *d)
+{
+    const TileConfig &t256 = kMfmaBf16Tiles[0], &t128 = kMfmaBf16Tiles[1],
+                     &t256x128 = kMfmaBf16Tiles[2];
+    if (tiles_of(d, t256) >= kNumCu / 2)
+        return t256;
+    if (tiles_of(d, t256x128) >= kNumCu / 2)
+        return t256x128;
+    return t128;
+}
+
+// Split-K slices for `tiles` output tiles: only when the tiles alone leave
+// most compute units idle and every slice keeps a long K range.
+int32_t auto_splits(const dg_gemm_desc *d, int64_t tiles)
+{
+    if (!reads_ab(d) || tiles >= kNumCu / 2 || d->K < 2048)
+        return 1;
+    int64_t s = kNumCu / tiles;                  // about one program per CU
+    int64_t by_k = d->K / 1024;                  // keep >= 1024 of K per slice
+    if (s > by_k) s = by_k;
+    if (s > 16) s = 16;
+    return s < 2 ? 1 : (int32_t)s;
+}
+
+dg_status make_plan(const dg_gemm_desc *d, const void *A, const void *B, size_t ws_avail,
+                    bool ws_known, Plan *plan)
+{
+    Plan p{};
+    const int32_t algo = d->algo;
+    if (algo == DG_ALGO_MFMA_F32)
+        return DG_ERROR_NOT_SUPPORTED;
+    if (algo == DG_ALGO_MFMA_BF16 || (algo == DG_ALGO_AUTO && mfma_bf16_eligible(d, A, B))) {
+        if (!mfma_bf16_eligible(d, A, B))
+            return DG_ERROR_NOT_SUPPORTED;
+        p.kernel = KERNEL_MFMA_BF16;
+        p.tile = pick_mfma_tile(d);
+    } else if (algo == DG_ALGO_VALU_F32 || (algo == DG_ALGO_AUTO && valu_eligible(d, A, B))) {
+        if (!valu_eligible(d, A, B))
+            return DG_ERROR_NOT_SUPPORTED;
+        p.kernel = KERNEL_VALU_F32;
+        p.tile = kValuTiles[0];
+    } else {
+        p.kernel = KERNEL_GENERIC;
+        p.tile = kGenericTiles[0];
+    }
+    const int64_t tiles = tiles_of(d, p.tile);
+    const int64_t plane = d->batch * d->M * d->N * (int64_t)sizeof(float);
+    int32_t S;
+    if (!reads_ab(d)) {
+        S = 1;
+    } else if (d->split_k >= 1) {
+        S = d->split_k;
+    } else {
+        S = auto_splits(d, tiles);
+        // the automatic choice never asks for more workspace than given
+        if (ws_known && S > 1 && (size_t)plane * S > ws_avail)
+            S = plane > 0 ? (int32_t)(ws_avail / (size_t)plane) : 1;
+        if (S < 2)
+            S = 1;
+    }
+    p.splits = S;
+    p.k_per_split = S > 1 ? ceil_div(ceil_div(d->K, S), p.tile.bk) * p.tile.bk : d->K;
+    if (p.k_per_split == 0)
+        p.k_per_split = 1;
+    p.workspace_bytes = S > 1 ? (size_t)plane * S : 0;
+    int64_t programs;
+    if (__builtin_mul_overflow(tiles, (int64_t)S, &programs) || programs > INT32_MAX ||
+        programs * p.tile.threads > (int64_t)UINT32_MAX)
+        return DG_ERROR_NOT_SUPPORTED;
+    p.programs = programs;
+    if (S > 1) {
+        int64_t total = d->batch * d->M * d->N;
+        int64_t blocks = ceil_div(total, 256);
+        p.reduce_blocks = blocks < 65536 ? blocks : 65536;
+    }
+    *plan = p;
+    return DG_SUCCESS;
+}
+
+void fill_args(const dg_gemm_desc *d, const Plan &p, const void *A, const void *B, void *C,
+               void *ws, GemmArgs *g)
+{
+    memset(g, 0, sizeof *g);
+    g->A = A;
+    g->B = B;
+    g->C = C;
+    g->bias = d->bias;
+    g->ws = (float *)ws;
+    g->M = d->M;
+    g->N = d->N;
+    g->K = d->K;
+    g->lda = d->lda;
+    g->ldb = d->ldb;
+    g->ldc = d->ldc;
+    g->sa = d->stride_a;
+    g->sb = d->stride_b;
+    g->sc = d->stride_c;
+    g->k_per_split = p.k_per_split;
+    g->alpha = d->alpha;
+    g->beta = d->beta;
+    g->a_col = d->a_order == DG_COL_MAJOR;
+    g->b_col = d->b_order == DG_COL_MAJOR;
+    g->c_col = d->c_order == DG_COL_MAJOR;
+    g->c_bf16 = d->c_type == DG_BF16;
+    g->bias_bf16 = d->bias_type == DG_BF16;
+    g->act = d->act;
+    g->write_partial = p.splits > 1;
+    g->ab_bf16 = d->a_type == DG_BF16;
+    g->sched.num_pid_m = ceil_div(d->M, p.tile.bm);
+    g->sched.num_pid_n = ceil_div(d->N, p.tile.bn);
+    g->sched.batch = d->batch;
+    g->sched.splits = p.splits;
+    g->sched.group_m = d->group_m > 0 ? d->group_m : kDefaultGroupM;
+    g->sched.xcd_remap = d->xcd_remap >= 0 ? 1 : 0;
+}
+
+const char *kernel_name(Kernel k)
+{
+    switch (k) {
+    case KERNEL_GENERIC: return "generic";
+    case KERNEL_VALU_F32: return "valu_f32";
+    case KERNEL_MFMA_BF16: return "mfma_bf16";
+    case KERNEL_MFMA_F32: return "mfma_f32";
+    }
+    return "?";
+}
+
+} // namespace
+
+extern "C" {
+
+int dg_version(void) { return DG_VERSION; }
+
+const char *dg_status_string(dg_status s)
+{
+    switch (s) {
+    case DG_SUCCESS: return "DG_SUCCESS";
+    case DG_ERROR_INVALID_VALUE: return "DG_ERROR_INVALID_VALUE";
+    case DG_ERROR_NOT_SUPPORTED: return "DG_ERROR_NOT_SUPPORTED";
+    case DG_ERROR_INSUFFICIENT_WORKSPACE: return "DG_ERROR_INSUFFICIENT_WORKSPACE";
+    case DG_ERROR_LAUNCH: return "DG_ERROR_LAUNCH";
+    }
+    return "DG_ERROR_UNKNOWN";
+}
+
+dg_status dg_gemm_workspace_size(const dg_gemm_desc *d, size_t *bytes)
+{
+    if (!bytes)
+        return DG_ERROR_INVALID_VALUE;
+    Extents e;
+    dg_status st = validate_desc(d, &e);
+    if (st != DG_SUCCESS)
+        return st;
+    *bytes = 0;
+    if (is_noop(d))
+        return DG_SUCCESS;
+    Plan p;
+    st = make_plan(d, nullptr, nullptr, 0, false, &p);
+    if (st != DG_SUCCESS)
+        return st;
+    *bytes = p.workspace_bytes;
+    return DG_SUCCESS;
+}
+
+dg_status dg_gemm_describe(const dg_gemm_desc *d, size_t workspace_bytes, char *buf, size_t len)
+{
+    if (!buf || len == 0)
+        return DG_ERROR_INVALID_VALUE;
+    Extents e;
+    dg_status st = validate_desc(d, &e);
+    if (st != DG_SUCCESS)
+        return st;
+    if (is_noop(d)) {
+        snprintf(buf, len, "noop");
+        return DG_SUCCESS;
+    }
+    Plan p;
+    st = make_plan(d, nullptr, nullptr, workspace_bytes, true, &p);
+    if (st != DG_SUCCESS)
+        return st;
+    snprintf(buf, len,
+             "kernel=%s tile=%s bm=%d bn=%d bk=%d threads=%d splits=%d k_per_split=%lld "
+             "programs=%lld group_m=%d xcd_remap=%d workspace=%zu",
+             kernel_name(p.kernel), p.tile.name, p.tile.bm, p.tile.bn, p.tile.bk, p.tile.threads,
+             p.splits, (long long)p.k_per_split, (long long)p.programs,
+             d->group_m > 0 ? d->group_m : kDefaultGroupM, d->xcd_remap >= 0 ? 1 : 0,
+             p.workspace_bytes);
+    return DG_SUCCESS;
+}
+
+dg_status dg_gemm(const dg_gemm_desc *d, const void *A, const void *B, void *C, void *workspace,
+                  size_t workspace_bytes, void *stream)
+{
+    Extents e;
+    dg_status st = validate_desc(d, &e);
+    if (st != DG_SUCCESS)
+        return st;
+    st = validate_ptrs(d, e, A, B, C);
+    if (st != DG_SUCCESS)
+        return st;
+    if (is_noop(d))
+        return DG_SUCCESS;
+    Plan p;
+    st = make_plan(d, A, B, workspace ? workspace_bytes : 0, true, &p);
+    if (st != DG_SUCCESS)
+        return st;
+    if (p.splits > 1) {
+        if (!workspace || workspace_bytes < p.workspace_bytes)
+            return DG_ERROR_INSUFFICIENT_WORKSPACE;
+        if (ranges_overlap(workspace, (int64_t)p.workspace_bytes, C, e.c_bytes))
+            return DG_ERROR_INVALID_VALUE;
+    }
+    GemmArgs g;
+    fill_args(d, p, A, B, C, workspace, &g);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t err = hipSuccess;
+    switch (p.kernel) {
+    case KERNEL_GENERIC: err = launch_generic(g, p, s); break;
+    case KERNEL_VALU_F32: err = launch_valu_f32(g, p, s); break;
+    case KERNEL_MFMA_BF16: err = launch_mfma_bf16(g, p, s); break;
+    default: return DG_ERROR_NOT_SUPPORTED;
+    }
+    if (err != hipSuccess)
+        return DG_ERROR_LAUNCH;
+    if (p.splits > 1) {
+        err = launch_splitk_reduce(g, p, s);
+        if (err != hipSuccess)
+            return DG_ERROR_LAUNCH;
+    }
+    return DG_SUCCESS;
+}
+
+dg_status dg_schedule_map(int64_t M, int64_t N, int64_t batch, int32_t split_k, int32_t bm,
+                          int32_t bn, int32_t group_m, int32_t xcd_remap, int32_t *out,
+                          int64_t out_len)
+{
+    if (M < 0 || N < 0 || batch < 0 || split_k < 1 || bm < 1 || bn < 1 || group_m < 0 ||
+        xcd_remap < -1 || xcd_remap > 1)
+        return DG_ERROR_INVALID_VALUE;
+    SchedArgs a{};
+    a.num_pid_m = ceil_div(M, bm);
+    a.num_pid_n = ceil_div(N, bn);
+    a.batch = batch;
+    a.splits = split_k;
+    a.group_m = group_m > 0 ? group_m : kDefaultGroupM;
+    a.xcd_remap = xcd_remap >= 0 ? 1 : 0;
+    const int64_t P = sched_programs(a);
+    if (P > 0 && (!out || out_len < 4 * P))
+        return DG_ERROR_INVALID_VALUE;
+    for (int64_t pid = 0; pid < P; ++pid) {
+        TileCoord c = decode_program(pid, a);
+        out[4 * pid + 0] = (int32_t)c.b;
+        out[4 * pid + 1] = c.s;
+        out[4 * pid + 2] = c.pid_m;
+        out[4 * pid + 3] = c.pid_n;
+    }
+    return DG_SUCCESS;
+}
+
+} // extern "C"

@@ -1,0 +1,158 @@
+// Generic LDS-tiled GEMM: every dtype pair, every operand order, any
+// leading dimension / alignment / batch stride, masked edges, split-K.
+//
+// This is the shared-memory tiling of "La GEMM, de zero a cuBLAS" section
+// 2.4 (cooperative tile loads with zero fill outside the matrix, barrier,
+// inner product over the staged tile, barrier) widened to a 4 x 4
+// register block per thread (section 2.6).  It is the correctness fallback
+// for shapes and layouts the specialised kernels do not take; fast paths
+// live in the VALU and MFMA kernel files.
+//
+// Tile 64 x 64 x 16, 256 threads.  Thread (tx, ty) owns rows ty + 16 i and
+// columns tx + 16 j, i, j < 4, so a wavefront reads 4 distinct A words
+// (broadcast) and 16 consecutive B words per LDS access.  Global loads walk
+// the operand's contiguous dimension with consecutive threads (coalescing,
+// section 2.3).  Loads are masked on the row / column index and on the K
+// range of the program's split ("Skill: Write a Triton GEMM Kernel",
+// Required reasoning process step 5): masked elements read as 0.
+#include "launch.hpp"
+
+namespace dg {
+
+namespace {
+
+constexpr int GBM = 64, GBN = 64, GBK = 16, GTHREADS = 256;
+
+template <bool A_BF16, bool B_BF16>
+__global__ __launch_bounds__(GTHREADS) void gemm_generic_kernel(GemmArgs g)
+{
+    __shared__ float As[GBK][GBM + 1];
+    __shared__ float Bs[GBK][GBN + 1];
+
+    const TileCoord tc = decode_program(blockIdx.x, g.sched);
+    const int64_t m0 = (int64_t)tc.pid_m * GBM;
+    const int64_t n0 = (int64_t)tc.pid_n * GBN;
+    int64_t kb, ke;
+    split_range(g, tc.s, kb, ke);
+
+    const int tid = threadIdx.x;
+    const int tx = tid % 16, ty = tid / 16;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = 0.0f;
+
+    if (g.alpha != 0.0f) {
+        const int64_t abase = tc.b * g.sa;
+        const int64_t bbase = tc.b * g.sb;
+        for (int64_t k0 = kb; k0 < ke; k0 += GBK) {
+            // A tile: 64 rows x 16 k.  Consecutive threads follow the
+            // contiguous dimension of A.
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int idx = tid + GTHREADS * e;
+                int mm, kk;
+                if (g.a_col) { mm = idx % GBM; kk = idx / GBM; }
+                else         { kk = idx % GBK; mm = idx / GBK; }
+                const int64_t gm = m0 + mm, gk = k0 + kk;
+                float v = 0.0f;
+                if (gm < g.M && gk < ke)
+                    v = load_as_f32(g.A, A_BF16, abase + elem_offset(g.a_col, g.lda, gm, gk));
+                As[kk][mm] = v;
+            }
+            // B tile: 16 k x 64 columns.
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int idx = tid + GTHREADS * e;
+                int nn, kk;
+                if (g.b_col) { kk = idx % GBK; nn = idx / GBK; }
+                else         { nn = idx % GBN; kk = idx / GBN; }
+                const int64_t gn = n0 + nn, gk = k0 + kk;
+                float v = 0.0f;
+                if (gn < g.N && gk < ke)
+                    v = load_as_f32(g.B, B_BF16, bbase + elem_offset(g.b_col, g.ldb, gk, gn));
+                Bs[kk][nn] = v;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < GBK; ++k) {
+                float a[4], b[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a[i] = As[k][ty + 16 * i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    b[j] = Bs[k][tx + 16 * j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+            }
+            __syncthreads();
+        }
+    }
+
+    // Store masked on M and N.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t gm = m0 + ty + 16 * i;
+        if (gm >= g.M)
+            continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t gn = n0 + tx + 16 * j;
+            if (gn < g.N)
+                write_result(g, tc.b, tc.s, gm, gn, acc[i][j]);
+        }
+    }
+}
+
+// Split-K reduction: for each output element, sum the S partials in split
+// order (a fixed order, so the result is reproducible), then apply the
+// epilogue exactly once.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int32_t splits)
+{
+    const int64_t total = g.sched.batch * g.M * g.N;
+    const int64_t plane = total;                  // one split's partials
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * 256) {
+        float sum = 0.0f;
+        for (int32_t s = 0; s < splits; ++s)
+            sum += g.ws[(int64_t)s * plane + e];
+        const int64_t n = e % g.N;
+        const int64_t bm = e / g.N;
+        const int64_t m = bm % g.M;
+        const int64_t b = bm / g.M;
+        store_c(g, b, m, n, epilogue_value(g, b, m, n, sum));
+    }
+}
+
+} // namespace
+
+const TileConfig kGenericTiles[] = {
+    {GBM, GBN, GBK, GTHREADS, 0, "generic_64x64x16"},
+};
+const int kNumGenericTiles = 1;
+
+hipError_t launch_generic(const GemmArgs &g, const Plan &p, hipStream_t stream)
+{
+    dim3 grid((unsigned)p.programs), block(GTHREADS);
+    // A and B share a dtype (validated on the host).
+    if (g.ab_bf16)
+        hipLaunchKernelGGL((gemm_generic_kernel<true, true>), grid, block, 0, stream, g);
+    else
+        hipLaunchKernelGGL((gemm_generic_kernel<false, false>), grid, block, 0, stream, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const GemmArgs &g, const Plan &p, hipStream_t stream)
+{
+    dim3 grid((unsigned)p.reduce_blocks), block(256);
+    hipLaunchKernelGGL(splitk_reduce_kernel, grid, block, 0, stream, g, p.splits);
+    return hipGetLastError();
+}
+
+} // namespace dg

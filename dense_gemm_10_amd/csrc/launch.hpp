@@ -1,0 +1,48 @@
+// Host-side plan and the launchers each kernel file provides.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace dg {
+
+enum Kernel {
+    KERNEL_GENERIC = 1,
+    KERNEL_VALU_F32 = 2,
+    KERNEL_MFMA_BF16 = 3,
+    KERNEL_MFMA_F32 = 4,
+};
+
+// One tile configuration of a kernel family.
+struct TileConfig {
+    int32_t bm, bn, bk;
+    int32_t threads;
+    int32_t variant;     // index into the family's instantiation table
+    const char *name;
+};
+
+struct Plan {
+    Kernel kernel;
+    TileConfig tile;
+    int32_t splits;          // >= 1
+    int64_t k_per_split;
+    int64_t programs;        // grid size of the main kernel
+    size_t workspace_bytes;  // 0 unless splits > 1
+    int64_t reduce_blocks;   // grid of the split-K reduction (0 if none)
+};
+
+// Launchers: enqueue the kernel on `stream`; return hipSuccess or the
+// launch error.
+hipError_t launch_generic(const GemmArgs &g, const Plan &p, hipStream_t stream);
+hipError_t launch_valu_f32(const GemmArgs &g, const Plan &p, hipStream_t stream);
+hipError_t launch_mfma_bf16(const GemmArgs &g, const Plan &p, hipStream_t stream);
+hipError_t launch_splitk_reduce(const GemmArgs &g, const Plan &p, hipStream_t stream);
+
+// Tile configurations of each family (defined next to the kernels).
+extern const TileConfig kGenericTiles[];
+extern const TileConfig kValuTiles[];
+extern const TileConfig kMfmaBf16Tiles[];
+extern const int kNumGenericTiles, kNumValuTiles, kNumMfmaBf16Tiles;
+
+} // namespace dg

@@ -1,0 +1,87 @@
+// Output-tile scheduler shared by every GEMM kernel and by the host-side
+// map check (dg_schedule_map).  Compiled for host and device from the same
+// source so the CPU test exercises exactly what the kernels run.
+//
+// A launch has P = batch * splits * T programs, T = num_pid_m * num_pid_n
+// output tiles of BM x BN (ceil-div counts, so ragged tiles are included:
+// "Skill: Write a Triton GEMM Kernel", Required reasoning process step 2
+// and the grid-size failure mode).  Program id -> (b, s, pid_m, pid_n) is
+// the composition of three bijections:
+//   1. XCD remap.  The hardware deals consecutive workgroup ids round-robin
+//      to the 8 XCDs of an MI355X, each with its own L2.  Program p runs on
+//      XCD x = p mod 8; it is given logical id x*q + min(x, r) + p/8 with
+//      q = P/8, r = P mod 8, so XCD x owns one contiguous run of logical ids
+//      and the grouped order below stays local to one L2.
+//   2. Decode of the logical id L: t = L mod T, then split s, then batch b
+//      (tiles of one (b, s) are consecutive).
+//   3. Group-M swizzle of t, written as on "Skill: Write a Triton GEMM
+//      Kernel", Required reasoning process step 2 ("GEMM Kernel
+//      Optimization", L2 Cache Grouping): groups of G tile rows are walked
+//      column by column so that consecutive programs share A row panels and
+//      B column panels.  As printed there, the row inside the group is
+//      t mod group_rows (not the offset inside the group); that is also a
+//      bijection and is kept literally.
+#pragma once
+#include <stdint.h>
+
+#ifdef __HIPCC__
+#define DG_HD __host__ __device__
+#else
+#define DG_HD
+#endif
+
+namespace dg {
+
+constexpr int kNumXcd = 8;
+
+struct SchedArgs {
+    int64_t num_pid_m, num_pid_n;  // output tiles along M and N
+    int64_t batch;
+    int32_t splits;                // split-K slices (>= 1)
+    int32_t group_m;               // >= 1
+    int32_t xcd_remap;             // 1 = on
+    int32_t pad_;
+};
+
+struct TileCoord {
+    int64_t b;
+    int32_t s;
+    int32_t pid_m;
+    int32_t pid_n;
+};
+
+DG_HD inline int64_t sched_programs(const SchedArgs &a)
+{
+    return a.batch * (int64_t)a.splits * a.num_pid_m * a.num_pid_n;
+}
+
+DG_HD inline int64_t xcd_remap(int64_t pid, int64_t P)
+{
+    int64_t x = pid % kNumXcd;
+    int64_t q = P / kNumXcd, r = P % kNumXcd;
+    return x * q + (x < r ? x : r) + pid / kNumXcd;
+}
+
+DG_HD inline TileCoord decode_program(int64_t pid, const SchedArgs &a)
+{
+    const int64_t T = a.num_pid_m * a.num_pid_n;
+    const int64_t P = a.batch * (int64_t)a.splits * T;
+    const int64_t L = a.xcd_remap ? xcd_remap(pid, P) : pid;
+    const int64_t t = L % T;
+    const int64_t bs = L / T;
+    TileCoord c;
+    c.s = (int32_t)(bs % a.splits);
+    c.b = bs / a.splits;
+    // group-M swizzle of the tile index t
+    const int64_t in_group = (int64_t)a.group_m * a.num_pid_n;
+    const int64_t group_id = t / in_group;
+    const int64_t first_m = group_id * a.group_m;
+    int64_t rows = a.num_pid_m - first_m;
+    if (rows > a.group_m)
+        rows = a.group_m;
+    c.pid_m = (int32_t)(first_m + t % rows);
+    c.pid_n = (int32_t)((t % in_group) / rows);
+    return c;
+}
+
+} // namespace dg

@@ -1,0 +1,199 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point include/densegemm.h declares, the Python struct mirrors the C layout,
+and every invalid descriptor is rejected on the host before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import dense_gemm_10_amd as dg
+import workloads as W
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "densegemm.h")
+
+# Fake, never-dereferenced device addresses: every call below returns during
+# host validation, before anything is enqueued.
+PA, PB, PC, PW = 0x100000, 0x200000, 0x300000, 0x400000
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point():
+    names = _declared_functions()
+    assert set(names) >= {"dg_gemm", "dg_gemm_workspace_size", "dg_gemm_describe",
+                          "dg_status_string", "dg_version", "dg_schedule_map"}
+    lib = ctypes.CDLL(dg.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", dg.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (dg_\w+)", out))
+    assert exported == set(names)
+
+
+def test_struct_layout_matches_header():
+    fields = [f for f, _ in dg.DgGemmDesc._fields_]
+    src = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"',
+           'int main(void) {', 'printf("%zu\\n", sizeof(dg_gemm_desc));']
+    for f in fields:
+        src.append(f'printf("%zu\\n", offsetof(dg_gemm_desc, {f}));')
+    src.append("return 0; }")
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(c, "w").write("\n".join(src))
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", c, "-o", exe], check=True)
+        vals = [int(v) for v in subprocess.run([exe], capture_output=True, text=True,
+                                               check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(dg.DgGemmDesc)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(dg.DgGemmDesc, f).offset == off, f
+
+
+def test_version_and_status_strings():
+    assert dg.dg_version() == 10000
+    for code, name in [(0, "DG_SUCCESS"), (1, "DG_ERROR_INVALID_VALUE"),
+                       (2, "DG_ERROR_NOT_SUPPORTED"), (3, "DG_ERROR_INSUFFICIENT_WORKSPACE"),
+                       (4, "DG_ERROR_LAUNCH")]:
+        assert dg.dg_status_string(code) == name
+    assert dg.dg_status_string(99) == "DG_ERROR_UNKNOWN"
+
+
+def _desc(**kw):
+    base = dict(M=64, N=48, K=32, a_type="f32")
+    base.update(kw)
+    return dg.make_desc(**base)
+
+
+def _gemm_status(d, A=PA, B=PB, C=PC, ws=None, ws_bytes=0):
+    return dg.dg_gemm(d, A, B, C, ws, ws_bytes, None, check=False)
+
+
+INVALID = [
+    ("negative M", dict(M=-1)),
+    ("negative K", dict(K=-3)),
+    ("negative batch", dict(batch=-1)),
+    ("bad a_type", dict(a_type=7)),
+    ("bad order", dict(a_order=2)),
+    ("bad act", dict(act=9)),
+    ("bad algo", dict(algo=11)),
+    ("negative split", dict(split_k=-1)),
+    ("negative group", dict(group_m=-2)),
+    ("bad xcd flag", dict(xcd_remap=3)),
+    ("lda below K (row-major A)", dict(lda=31)),
+    ("lda below M (col-major A)", dict(a_order="col", lda=63)),
+    ("ldb below N (row-major B)", dict(ldb=47)),
+    ("ldb below K (col-major B)", dict(b_order="col", ldb=31)),
+    ("ldc below N", dict(ldc=47)),
+    ("ldc below M (col-major C)", dict(c_order="col", ldc=63)),
+    ("zero ld", dict(lda=0)),
+    ("negative stride", dict(stride_a=-8)),
+    ("C batches overlap", dict(batch=2, stride_c=100)),
+    ("C broadcast", dict(batch=2, stride_c=0)),
+    ("size overflow", dict(M=2 ** 40, N=2 ** 40, K=1, lda=1, ldb=2 ** 40, ldc=2 ** 40)),
+]
+
+
+@pytest.mark.parametrize("what,kw", INVALID, ids=[w for w, _ in INVALID])
+def test_invalid_descriptors_rejected_before_launch(what, kw):
+    d = _desc(**kw)
+    assert _gemm_status(d) == dg.DG_ERROR_INVALID_VALUE
+    with pytest.raises(dg.DgError) as e:
+        dg.dg_gemm_workspace_size(d)
+    assert e.value.status == dg.DG_ERROR_INVALID_VALUE
+
+
+def test_bad_struct_size():
+    d = _desc()
+    d.struct_size = 12
+    assert _gemm_status(d) == dg.DG_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("kw", [dict(a_type="f32", b_type="bf16"),
+                                dict(a_type="bf16", b_type="f32"),
+                                dict(a_type="f32", c_type="bf16"),
+                                dict(split_k=100000)])
+def test_unsupported_combinations(kw):
+    assert _gemm_status(_desc(**kw)) == dg.DG_ERROR_NOT_SUPPORTED
+
+
+def test_pointer_rules():
+    d = _desc()
+    assert _gemm_status(d, C=None) == dg.DG_ERROR_INVALID_VALUE
+    assert _gemm_status(d, A=None) == dg.DG_ERROR_INVALID_VALUE
+    assert _gemm_status(d, B=None) == dg.DG_ERROR_INVALID_VALUE
+    assert _gemm_status(d, A=PA + 2) == dg.DG_ERROR_INVALID_VALUE    # fp32 needs 4-byte alignment
+    bd = _desc(a_type="bf16")
+    assert _gemm_status(bd, C=PC + 1) == dg.DG_ERROR_INVALID_VALUE
+    # C overlapping A or B
+    assert _gemm_status(d, C=PA + 4) == dg.DG_ERROR_INVALID_VALUE
+    assert _gemm_status(d, C=PB - 16) == dg.DG_ERROR_INVALID_VALUE
+    # C overlapping the bias vector
+    dbias = _desc(bias=PC + 8)
+    assert _gemm_status(dbias) == dg.DG_ERROR_INVALID_VALUE
+
+
+def test_noop_shapes_succeed_without_launch():
+    for kw in [dict(M=0), dict(N=0), dict(batch=0)]:
+        d = _desc(**kw)
+        assert _gemm_status(d, A=None, B=None, C=None) == dg.DG_SUCCESS
+        assert dg.dg_gemm_workspace_size(d) == 0
+        assert dg.dg_gemm_describe(d) == "noop"
+
+
+def test_forced_split_needs_workspace():
+    d = _desc(K=4096, split_k=4)
+    need = dg.dg_gemm_workspace_size(d)
+    assert need == 4 * 64 * 48 * 4
+    assert _gemm_status(d) == dg.DG_ERROR_INSUFFICIENT_WORKSPACE
+    assert _gemm_status(d, ws=PW, ws_bytes=need - 4) == dg.DG_ERROR_INSUFFICIENT_WORKSPACE
+    # workspace overlapping C
+    assert _gemm_status(d, ws=PC, ws_bytes=need) == dg.DG_ERROR_INVALID_VALUE
+
+
+def _desc_for(p, **kw):
+    f = W.desc_fields(p)
+    f.update(kw)
+    return dg.make_desc(**f)
+
+
+def test_plans_of_the_five_workloads():
+    c1 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c1"]))
+    assert "kernel=valu_f32" in c1 and "splits=1" in c1
+    c2 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c2"]))
+    assert "kernel=valu_f32" in c2 and "programs=1024" in c2
+    c3 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c3"]))
+    assert "kernel=mfma_bf16" in c3 and "bm=256 bn=256" in c3 and "programs=256" in c3
+    c4 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c4"]))
+    assert "kernel=mfma_bf16" in c4
+    d5 = _desc_for(W.WORKLOADS["c5"])
+    ws = dg.dg_gemm_workspace_size(d5)
+    assert ws > 0
+    c5 = dg.dg_gemm_describe(d5, ws)
+    assert "kernel=mfma_bf16" in c5 and "splits=1 " not in c5
+    # without workspace the automatic choice does not split
+    assert "splits=1 " in dg.dg_gemm_describe(d5, 0)
+
+
+def test_layouts_outside_the_fast_paths_use_the_generic_kernel():
+    assert "kernel=generic" in dg.dg_gemm_describe(_desc(lda=33))     # ld not a multiple of 4
+    assert "kernel=generic" in dg.dg_gemm_describe(
+        _desc(a_type="bf16", a_order="col"))                          # bf16 A not K-contiguous
+    d = _desc(a_type="bf16", b_order="col", lda=36)                    # lda not a multiple of 8
+    assert "kernel=generic" in dg.dg_gemm_describe(d)
+    with pytest.raises(dg.DgError) as e:
+        dg.dg_gemm_describe(_desc(a_type="bf16", algo=dg.DG_ALGO_MFMA_BF16))
+    assert e.value.status == dg.DG_ERROR_NOT_SUPPORTED
+
+
+def test_k_zero_and_alpha_zero_never_split():
+    assert "splits=1 " in dg.dg_gemm_describe(_desc(K=0, split_k=8, lda=1), 1 << 30)
+    assert "splits=1 " in dg.dg_gemm_describe(_desc(K=8192, alpha=0.0, split_k=8), 1 << 30)

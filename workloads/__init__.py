@@ -227,6 +227,14 @@ def _fill_value(dtype, fill):
     return to_storage(np.array([fill], np.float32), BF16)[0]
 
 
+def _strided_view(buf, order, ld, base, rows, cols):
+    """Writable view of one rows x cols matrix starting at element ``base``."""
+    item = buf.itemsize
+    strides = (ld * item, item) if order == ROW else (item, ld * item)
+    return np.lib.stride_tricks.as_strided(buf[base:], shape=(rows, cols), strides=strides,
+                                           writeable=True)
+
+
 def lay_out(logical, order, ld, stride, n_elems, dtype, fill=None):
     """Place logical matrices [batch][rows][cols] (storage dtype) into a flat
     buffer with the given order / ld / batch stride.  Positions not covered
@@ -234,11 +242,10 @@ def lay_out(logical, order, ld, stride, n_elems, dtype, fill=None):
     tests see stray reads)."""
     buf = np.full(n_elems, _fill_value(dtype, fill), dtype=storage_dtype(dtype))
     batch, rows, cols = logical.shape
-    r = np.arange(rows)[:, None]
-    c = np.arange(cols)[None, :]
-    off = (r * ld + c) if order == ROW else (c * ld + r)
+    if n_elems == 0 or rows == 0 or cols == 0:
+        return buf
     for b in range(batch):
-        buf[b * stride + off] = logical[b]
+        _strided_view(buf, order, ld, b * stride, rows, cols)[...] = logical[b]
         if stride == 0:
             break
     return buf
@@ -246,12 +253,11 @@ def lay_out(logical, order, ld, stride, n_elems, dtype, fill=None):
 
 def read_back(buf, order, ld, stride, batch, rows, cols):
     """Inverse of lay_out: gather logical [batch][rows][cols] from a buffer."""
-    r = np.arange(rows)[:, None]
-    c = np.arange(cols)[None, :]
-    off = (r * ld + c) if order == ROW else (c * ld + r)
     out = np.empty((batch, rows, cols), dtype=buf.dtype)
+    if rows == 0 or cols == 0:
+        return out
     for b in range(batch):
-        out[b] = buf[b * stride + off]
+        out[b] = _strided_view(buf, order, ld, b * stride, rows, cols)
     return out
 
 
@@ -318,3 +324,13 @@ def sample_points(p: Problem, n, seed=12345):
     return (np.concatenate([cb, b]).astype(np.int64),
             np.concatenate([ci, i]).astype(np.int64),
             np.concatenate([cj, j]).astype(np.int64))
+
+
+def desc_fields(p: Problem):
+    """The descriptor fields of a Problem, as plain values (names follow the
+    library's descriptor)."""
+    return dict(M=p.M, N=p.N, K=p.K, batch=p.batch, a_type=p.a_type, b_type=p.b_type,
+                c_type=p.c_type, a_order=p.a_order, b_order=p.b_order, c_order=p.c_order,
+                lda=p.lda_, ldb=p.ldb_, ldc=p.ldc_, stride_a=p.stride_a_,
+                stride_b=p.stride_b_, stride_c=p.stride_c_, alpha=p.alpha, beta=p.beta,
+                bias_type=p.bias_type, act=p.act, split_k=p.split_k)
