@@ -85,6 +85,29 @@ def time_workload(name, steps, warmup, **desc_overrides):
                 kernel=plan.split()[0].split("=")[1])
 
 
+def time_copy(steps, warmup, nbytes=512 << 20):
+    """Plain device-to-device copy of nbytes (torch's copy kernel): the
+    reference for the achievable HBM rate and for scaling the FETCH_SIZE /
+    WRITE_SIZE counters (it reads and writes exactly nbytes per step)."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        dst.copy_(src)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms,
+            "gbps_read_plus_write": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(name, budget_s=12.0):
     """Oracle throughput on a seeded sample of the workload's outputs."""
     import numpy as np
@@ -115,7 +138,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "copy"])
     ap.add_argument("--secondary", default="c3",
                     help="second workload reported in the same line ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -135,6 +158,11 @@ def main():
         sys.exit(1)
     import dense_gemm_10_amd as dg
     from dense_gemm_10_amd import accounting as acc
+
+    if args.workload == "copy":
+        r = time_copy(args.steps, args.warmup)
+        print(json.dumps({"workload": "copy_512MiB", **r}), flush=True)
+        return
 
     overrides = dict(algo=args.algo, group_m=args.group_m, xcd_remap=args.xcd_remap)
     main_r = time_workload(args.workload, args.steps, args.warmup, **overrides)
