@@ -115,7 +115,7 @@ def cpu_baseline(name, budget_s=12.0):
     import workloads as W
     p = W.WORKLOADS[name]
     x = W.make_inputs(p)
-    pb, pi, pj = W.sample_points(p, 4_000_000, seed=777)
+    pb, pi, pj = W.sample_points(p, 8_000_000, seed=777)
     done, chunk, t0 = 0, 2048, time.perf_counter()
     while done < pb.size:
         sl = slice(done, min(done + chunk, pb.size))

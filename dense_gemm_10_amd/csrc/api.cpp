@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/densegemm.h"
@@ -177,8 +178,10 @@ bool mfma_bf16_eligible(const dg_gemm_desc *d, const void *A, const void *B)
 {
     if (d->a_type != DG_BF16 || d->a_order != DG_ROW_MAJOR || d->b_order != DG_COL_MAJOR)
         return false;
+    // the kernel addresses a tile with 32-bit byte offsets: 256 rows * ld * 2 < 2^31
     return aligned_to(A, 16) && aligned_to(B, 16) && d->lda % 8 == 0 && d->ldb % 8 == 0 &&
-           d->stride_a % 8 == 0 && d->stride_b % 8 == 0;
+           d->stride_a % 8 == 0 && d->stride_b % 8 == 0 && d->lda < (1 << 22) &&
+           d->ldb < (1 << 22);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -188,16 +191,35 @@ int64_t tiles_of(const dg_gemm_desc *d, const TileConfig &t)
     return ceil_div(d->M, t.bm) * ceil_div(d->N, t.bn) * d->batch;
 }
 
-// Pick the bf16 MFMA tile: the largest tile that keeps at least about
-// half of the compute units busy.
+// Tile named by the DG_FORCE_TILE environment variable (benchmarking and
+// ablation only), or NULL.
+const TileConfig *forced_tile(const TileConfig *table, int n)
+{
+    const char *want = getenv("DG_FORCE_TILE");
+    if (!want || !*want)
+        return nullptr;
+    for (int i = 0; i < n; ++i)
+        if (strcmp(table[i].name, want) == 0)
+            return &table[i];
+    return nullptr;
+}
+
+// Pick the bf16 MFMA tile.  The 256 x 256 tile (one workgroup per CU) has
+// the best flop-per-byte ratio but quantises badly when its tile count is
+// not close to a whole number of waves over the 256 CUs ("La GEMM, de zero
+// a cuBLAS", section 2.10 on wave quantisation): e.g. 4095 x 4097 gives 272
+// tiles = 1.06 waves.  It is used only when the waves it forms are at least
+// 85 % full; otherwise the 128 x 128 tile (two workgroups per CU, 4x the
+// tiles) is used.
 TileConfig pick_mfma_tile(const dg_gemm_desc *d)
 {
-    const TileConfig &t256 = kMfmaBf16Tiles[0], &t128 = kMfmaBf16Tiles[1],
-                     &t256x128 = kMfmaBf16Tiles[2];
-    if (tiles_of(d, t256) >= kNumCu / 2)
+    if (const TileConfig *f = forced_tile(kMfmaBf16Tiles, kNumMfmaBf16Tiles))
+        return *f;
+    const TileConfig &t256 = kMfmaBf16Tiles[0], &t128 = kMfmaBf16Tiles[1];
+    const int64_t tiles = tiles_of(d, t256);
+    const int64_t waves = ceil_div(tiles, kNumCu);
+    if (tiles >= kNumCu && tiles * 100 >= waves * kNumCu * 85)
         return t256;
-    if (tiles_of(d, t256x128) >= kNumCu / 2)
-        return t256x128;
     return t128;
 }
 

@@ -3,35 +3,48 @@
 //
 // The structure is the tiled blocked GEMM of "GEMM Kernel Optimization"
 // (Core Technique: one workgroup per BM x BN output tile, K walked in
-// BK chunks, fp32 accumulators, cast on store) with the matrix-core
-// inner loop of its "Tensor Core Utilization" section and the three tiling
-// levels of "La GEMM, de zero a cuBLAS" (workgroup tile in LDS, wave tile
-// in registers, 32 x 32 x 16 MFMA fragments).
+// BK chunks, fp32 accumulators, cast on store) with the matrix-core inner
+// loop of its "Tensor Core Utilization" section and the three tiling levels
+// of "La GEMM, de zero a cuBLAS" (workgroup tile in LDS, wave tile in
+// registers, 32 x 32 x 16 MFMA fragments).  The multi-stage ring below is
+// the double buffering of that page's section 2.8 taken further.
 //
 // Operands: A row-major (M x K) and B column-major (K x N), i.e. both with
 // K contiguous, which is the order an MFMA lane consumes: lane l supplies 8
 // consecutive k of row (l mod 32) of A and of column (l mod 32) of B.
 //
-// Data path per K tile (BK = 64):
-//   global -> registers: 16-byte loads, 8 consecutive threads cover one
-//     128-byte row of the tile (coalesced), masked on the row bound and the
-//     split's K range with zero fill;
-//   registers -> LDS: row r's 16-byte chunk c is stored at chunk position
-//     c ^ ((r / 2) mod 8) (XOR swizzle).  LDS serves a 128-bit access 16
-//     lanes at a time across 256 bytes of banks; 16 lanes reading 16
-//     consecutive rows at one logical chunk, or 16 lanes writing two
-//     consecutive rows, then touch 16 different 16-byte bank groups;
-//   LDS -> registers: ds_read_b128 fragments, 4 k-steps of 16 per tile;
+// Data path:
+//   global -> LDS: direct DMA (global_load_lds_dwordx4): each instruction
+//     moves 64 x 16 bytes, lane l's 16 bytes landing at LDS address
+//     M0 + 16 l, without passing through registers.  A K tile (BK = 32) of
+//     A and of B is a "stage"; NSTAGE stages form a ring and the loads of
+//     tile t + NSTAGE - 1 are issued while tile t is multiplied, so each
+//     load has NSTAGE - 1 tiles of MFMA work to arrive in.
+//   LDS layout: a stage row (one row of A, or one column of B) is 64 bytes
+//     = 4 chunks of 8 bf16; logical chunk c of row r is stored at slot
+//     c ^ ((r / 4) mod 4).  The LDS serves a 128-bit access 16 lanes at a
+//     time over 256 bytes of banks; 16 lanes reading one logical chunk of
+//     16 consecutive rows then hit 16 different 16-byte bank groups.  The
+//     DMA lanes are assigned so that consecutive lanes fill consecutive
+//     slots: lane l loads the global chunk that belongs in slot l.
+//   LDS -> registers: ds_read_b128 fragments, 2 k-steps of 16 per stage;
 //   MFMA: each wavefront owns a TM x TN wave tile = FM x FN blocks of
 //     32 x 32, accumulated in FM*FN*16 fp32 registers per lane.
-// The next tile is fetched into registers while the current one is
-// multiplied, then written to the other LDS buffer: two LDS stages, one
-// barrier per K tile ("La GEMM, de zero a cuBLAS", section 2.8).
+// The DMA is issued through inline assembly so that the compiler does not
+// serialise it: vector-memory loads of a wave complete in order, so waiting
+// until at most (NSTAGE - 2) tiles' loads are outstanding (s_waitcnt
+// vmcnt), then one workgroup barrier, makes a stage readable and the stage
+// read in the previous iteration writable.
+//
+// A partial last K tile (K not a multiple of BK) is loaded first, through
+// registers with a K mask, so the steady-state loop is uniform.  Rows past
+// M (or N) are clamped to the last row: the loads stay inside the matrix
+// and those rows only feed outputs that are never stored.
 //
 // Requirements checked on the host: bf16 A (row-major) and B (column-
 // major); 16-byte aligned base pointers; lda, ldb and the batch strides
-// multiples of 8 elements.  K may be anything (the last chunk is masked
-// element by element).
+// multiples of 8 elements; BM * lda and BN * ldb small enough for 32-bit
+// byte offsets inside a tile.
 #include "launch.hpp"
 
 namespace dg {
@@ -41,12 +54,44 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int MBK = 64;   // K per LDS tile: 8 chunks of 8 bf16 per row
+constexpr int MBK = 32;      // K per stage: 4 chunks of 8 bf16 per row
+
+// s_waitcnt immediate: wait until at most n vector-memory loads of this
+// wave are outstanding and all its LDS operations have completed (expcnt
+// left unconstrained).
+constexpr int vm_lgkm0_imm(int n)
+{
+    return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (0 << 8);
+}
+
+// A value that is the same in every lane, moved to scalar registers (the
+// compiler cannot prove uniformity of results of 64-bit divisions).
+__device__ __forceinline__ int64_t uniform_i64(int64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ const void *uniform_ptr(const void *p)
+{
+    return (const void *)uniform_i64((int64_t)(uintptr_t)p);
+}
+
+// One DMA instruction: 16 bytes per lane from base + voff (bytes) into LDS
+// at lds_addr + 16 * lane.  lds_addr must be wave-uniform.
+__device__ __forceinline__ void dma_16(const void *base, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "memory", "m0");
+}
 
 // 8 bf16 of one row at k = k_first .. k_first+7, zero for k >= ke (the
-// K-boundary mask of the last, partial K tile).  `row` points at k = 0 of
-// the row; ke >= 1.  Branch-free: the index is clamped to ke-1, so every
-// load stays inside the row, and masked elements are replaced by 0.
+// K-boundary mask of a partial K tile).  `row` points at k = 0 of the row;
+// ke >= 1.  Branch-free: the index is clamped to ke-1, so every load stays
+// inside the row, and masked elements are replaced by 0.
 __device__ __forceinline__ uint4 load_chunk_tail(const uint16_t *row, int64_t k_first,
                                                  int64_t ke)
 {
@@ -170,37 +215,101 @@ __device__ __forceinline__ void store_chunk(const GemmArgs &g, const TileCoord &
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int kStages>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g)
 {
     constexpr int NT = 64 * WM * WN;
+    constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;    // wave tile
     constexpr int FM = TM / 32, FN = TN / 32;    // 32x32 blocks per wave
-    constexpr int ROWS_PER_PASS = NT / 8;        // tile rows loaded per pass
-    constexpr int ACH = BM / ROWS_PER_PASS;      // 16-byte chunks per thread (A)
-    constexpr int BCH = BN / ROWS_PER_PASS;      // (B)
-    constexpr int A_STAGE = BM * 8, B_STAGE = BN * 8;   // uint4 per stage
+    constexpr int ROWS = BM + BN;                // stage rows: A rows, then B columns
+    constexpr int GROUPS = ROWS / 16;            // DMA instructions (16 rows each) per stage
+    constexpr int LPW = GROUPS / NW;             // ... per wave
+    constexpr int STAGE_SLOTS = ROWS * 4;        // 16-byte slots per stage
+    constexpr int D = kStages - 1;               // prefetch distance (tiles)
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
-    static_assert(BM % ROWS_PER_PASS == 0 && BN % ROWS_PER_PASS == 0, "load split");
+    static_assert(BM % 16 == 0 && BN % 16 == 0 && GROUPS % NW == 0, "DMA split");
 
     extern __shared__ uint4 lds[];
-    uint4 *As = lds;                  // [2][BM rows][8 chunks]
-    uint4 *Bs = lds + 2 * A_STAGE;    // [2][BN cols][8 chunks]
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)lds;
 
-    const TileCoord tc = decode_program(blockIdx.x, g.sched);
+    TileCoord tc = decode_program(blockIdx.x, g.sched);
+    tc.b = uniform_i64(tc.b);
+    tc.s = __builtin_amdgcn_readfirstlane(tc.s);
+    tc.pid_m = __builtin_amdgcn_readfirstlane(tc.pid_m);
+    tc.pid_n = __builtin_amdgcn_readfirstlane(tc.pid_n);
     const int64_t m0 = (int64_t)tc.pid_m * BM;
     const int64_t n0 = (int64_t)tc.pid_n * BN;
     int64_t kb, ke;
     split_range(g, tc.s, kb, ke);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int wm = wave / WN, wn = wave % WN;
-    const int kc = tid & 7;          // chunk column this thread loads
-    const int r0 = tid >> 3;         // first tile row this thread loads
-    const uint16_t *A = (const uint16_t *)g.A + tc.b * g.sa;
-    const uint16_t *B = (const uint16_t *)g.B + tc.b * g.sb;
     const int64_t M = g.M, N = g.N, lda = g.lda, ldb = g.ldb;
+    const uint16_t *A_tile = (const uint16_t *)g.A + tc.b * g.sa + m0 * lda;
+    const uint16_t *B_tile = (const uint16_t *)g.B + tc.b * g.sb + n0 * ldb;
+
+    // This lane's DMA sources: group q = wave * LPW + i covers stage rows
+    // 16q .. 16q+15 (A rows first, then B columns); lane l fills slot
+    // 64q + l = (row 16q + l/4, physical chunk l%4), i.e. logical chunk
+    // (l%4) ^ ((row/4)%4).  Byte offsets are relative to the tile's first
+    // row and K position; rows past the matrix are clamped.
+    uint32_t voff[LPW];
+    bool from_a[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int q = wave * LPW + i;
+        const int srow = q * 16 + lane / 4;           // stage row
+        const int c = (lane & 3) ^ ((srow >> 2) & 3); // logical chunk
+        from_a[i] = q * 16 < BM;                      // per group, hence wave-uniform
+        int64_t r = from_a[i] ? srow : srow - BM;     // row inside the A / B tile
+        const int64_t lim = from_a[i] ? M - m0 : N - n0;
+        r = r < lim ? r : lim - 1;
+        voff[i] = (uint32_t)((r * (from_a[i] ? lda : ldb) + c * 8) * 2);
+    }
+
+    // K position of virtual tile v: a partial tile (if any) comes first.
+    const int64_t klen = ke > kb ? ke - kb : 0;
+    const int64_t nfull = klen / MBK;
+    const bool tail = (klen % MBK) != 0;
+    const int64_t ntiles = nfull + (tail ? 1 : 0);
+    auto tile_k0 = [&](int64_t v) -> int64_t {
+        if (tail)
+            return v == 0 ? kb + nfull * MBK : kb + (v - 1) * MBK;
+        return kb + v * MBK;
+    };
+
+    // DMA instruction i (of LPW) of full tile v into its stage.
+    auto issue_dma_one = [&](int64_t v, int i) {
+        const int64_t k0 = tile_k0(v);
+        const uint32_t stage_addr = lds_base + (uint32_t)((v % kStages) * STAGE_SLOTS * 16);
+        const int q = wave * LPW + i;
+        dma_16(uniform_ptr((from_a[i] ? A_tile : B_tile) + k0), voff[i],
+               stage_addr + (uint32_t)(q * 64 * 16));
+    };
+    auto issue_dma = [&](int64_t v) {
+#pragma unroll
+        for (int i = 0; i < LPW; ++i)
+            issue_dma_one(v, i);
+    };
+
+    // The partial tile: same slots as the DMA, through registers, with the
+    // K mask.
+    auto load_tail = [&](int64_t v) {
+        const int64_t k0 = tile_k0(v);
+        uint4 *stage = lds + (v % kStages) * STAGE_SLOTS;
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int q = wave * LPW + i;
+            const int srow = q * 16 + lane / 4;
+            const int c = (lane & 3) ^ ((srow >> 2) & 3);
+            const uint16_t *rowp = (const uint16_t *)((const char *)(from_a[i] ? A_tile : B_tile) +
+                                                      voff[i]) - c * 8;
+            stage[q * 64 + lane] = load_chunk_tail(rowp, k0 + c * 8, ke);
+        }
+    };
 
     f32x16_t acc[FM][FN];
 #pragma unroll
@@ -211,74 +320,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
             for (int v = 0; v < 16; ++v)
                 acc[i][j][v] = 0.0f;
 
-    // Per-thread source pointers of the rows this thread loads.  Rows past
-    // M (or N) are clamped to the last row: the loads stay inside the
-    // matrix and those rows only feed outputs that are never stored.
-    const uint16_t *ap[ACH];
-    const uint16_t *bp[BCH];
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-        int64_t gm = m0 + r0 + i * ROWS_PER_PASS;
-        gm = gm < M ? gm : M - 1;
-        ap[i] = A + gm * lda + kc * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-        int64_t gn = n0 + r0 + i * ROWS_PER_PASS;
-        gn = gn < N ? gn : N - 1;
-        bp[i] = B + gn * ldb + kc * 8;
-    }
-
-    uint4 ra[ACH], rb[BCH];
-
-    // Full K tile: plain 16-byte loads, no predicates.
-    auto load_tiles_full = [&](int64_t k0) {
-#pragma unroll
-        for (int i = 0; i < ACH; ++i)
-            ra[i] = *(const uint4 *)(ap[i] + k0);
-#pragma unroll
-        for (int i = 0; i < BCH; ++i)
-            rb[i] = *(const uint4 *)(bp[i] + k0);
-    };
-    // Last, partial K tile: elements at k >= ke read as 0 (K-boundary mask).
-    auto load_tiles_tail = [&](int64_t k0) {
-        const int64_t gk = k0 + kc * 8;
-#pragma unroll
-        for (int i = 0; i < ACH; ++i)
-            ra[i] = load_chunk_tail(ap[i] - kc * 8, gk, ke);
-#pragma unroll
-        for (int i = 0; i < BCH; ++i)
-            rb[i] = load_chunk_tail(bp[i] - kc * 8, gk, ke);
-    };
-
-    auto store_tiles = [&](int st) {
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            const int r = r0 + i * ROWS_PER_PASS;
-            As[st * A_STAGE + r * 8 + (kc ^ ((r >> 1) & 7))] = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < BCH; ++i) {
-            const int r = r0 + i * ROWS_PER_PASS;
-            Bs[st * B_STAGE + r * 8 + (kc ^ ((r >> 1) & 7))] = rb[i];
-        }
-    };
-
     const int frag_row = lane & 31;       // row of A / column of B this lane feeds
     const int frag_half = lane >> 5;      // which 8 of the 16 k of one MFMA step
-    const int swz = (frag_row >> 1) & 7;  // swizzle key of the fragment row (wave tiles are 32-aligned)
+    const int swz = (frag_row >> 2) & 3;  // swizzle key (wave tiles are 32-aligned)
 
-    // Fragments of one 16-deep k step: FM blocks of A, FN blocks of B.
+    // Fragments of k-step ks (0 or 1) of a stage.
     auto load_frags = [&](int st, int ks, bf16x8_t *af, bf16x8_t *bf) {
-        const uint4 *as = As + st * A_STAGE + (wm * TM + frag_row) * 8;
-        const uint4 *bs = Bs + st * B_STAGE + (wn * TN + frag_row) * 8;
+        const uint4 *as = lds + st * STAGE_SLOTS + (wm * TM + frag_row) * 4;
+        const uint4 *bs = lds + st * STAGE_SLOTS + (BM + wn * TN + frag_row) * 4;
         const int c = (ks * 2 + frag_half) ^ swz;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            af[i] = __builtin_bit_cast(bf16x8_t, as[i * 32 * 8 + c]);
+            af[i] = __builtin_bit_cast(bf16x8_t, as[i * 32 * 4 + c]);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            bf[j] = __builtin_bit_cast(bf16x8_t, bs[j * 32 * 8 + c]);
+            bf[j] = __builtin_bit_cast(bf16x8_t, bs[j * 32 * 4 + c]);
     };
 
     auto mfma_step = [&](const bf16x8_t *af, const bf16x8_t *bf) {
@@ -289,59 +345,48 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     };
 
-    // Fragment registers, two sets.  fa[1]/fb[1] carry the last k step of
-    // the previous tile into the next iteration: its 16 MFMAs run after the
-    // barrier, while the first fragment reads of the new tile are in flight.
+    // Two fragment register sets; fa[1]/fb[1] carry k-step 1 of a stage
+    // into the next iteration, whose MFMAs run after the barrier while the
+    // new stage's first fragments are being read.
     bf16x8_t fa[2][FM], fb[2][FN];
 
-    // One LDS stage: the deferred step of the previous tile, then k steps
-    // 0..2 of this tile, each while the next step's fragments are read;
-    // step 3's fragments are left in fa[1]/fb[1].
-    auto tile_body = [&](int st) {
+    // One stage: k-step 0's fragments are read first, then (in the steady
+    // state) the DMA of a later tile is issued, then the deferred MFMAs run
+    // while those reads land, then k-step 1's fragments are read while
+    // k-step 0's MFMAs run.
+    // The DMA instructions are spread over the deferred MFMAs (one after
+    // every MFMA_PER_DMA of them): a burst of DMA issues can stall the wave
+    // on a full memory queue while the matrix pipe runs dry.
+    constexpr int MFMA_PER_DMA = (FM * FN) / LPW > 0 ? (FM * FN) / LPW : 1;
+    auto stage_body = [&](int st, bool dma, int64_t v_dma) {
         load_frags(st, 0, fa[0], fb[0]);
-        mfma_step(fa[1], fb[1]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], acc[i][j],
+                                                                    0, 0, 0);
+                const int n = i * FN + j;
+                if (dma && (n % MFMA_PER_DMA) == MFMA_PER_DMA - 1 && n / MFMA_PER_DMA < LPW) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue_dma_one(v_dma, n / MFMA_PER_DMA);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         load_frags(st, 1, fa[1], fb[1]);
         mfma_step(fa[0], fb[0]);
-        load_frags(st, 2, fa[0], fb[0]);
-        mfma_step(fa[1], fb[1]);
-        load_frags(st, 3, fa[1], fb[1]);
-        mfma_step(fa[0], fb[0]);
     };
 
-    // Instruction order of one steady-state iteration (after its global
-    // loads): the first k step's fragment reads, then every MFMA paired with
-    // one LDS read of the following step's fragments, and in the last
-    // computed step every MFMA paired with one LDS write of the next tile,
-    // so the matrix pipe does not wait on LDS traffic it could overlap.
-    auto schedule_main_loop = [&]() {
-        constexpr int kMfma = 0x008, kDsRead = 0x100, kDsWrite = 0x200;
-        constexpr int kFrags = FM + FN, kMfmaPerStep = FM * FN;
-        constexpr int kWrites = ACH + BCH;
-        __builtin_amdgcn_sched_group_barrier(kDsRead, kFrags, 0);
-#pragma unroll
-        for (int step = 0; step < 3; ++step) {
-#pragma unroll
-            for (int i = 0; i < kMfmaPerStep; ++i) {
-                __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-                if (i < kFrags)
-                    __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < kMfmaPerStep; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-            if (i < kWrites)
-                __builtin_amdgcn_sched_group_barrier(kDsWrite, 1, 0);
-        }
+    // Barrier that the compiler may not move LDS accesses across.  It is
+    // always preceded by a wait for this wave's LDS reads (lgkmcnt 0), so a
+    // stage that any wave still reads is never the target of a DMA issued
+    // after the barrier.
+    auto barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // K loop.  The steady-state loop runs while the next tile is a full
-    // one; the last tile (partial when K is not a multiple of BK) is
-    // loaded with the masked loader in the short loop after it, so the
-    // steady state carries no predicates.
-    const int64_t klen = ke > kb ? ke - kb : 0;
-    const int64_t ntiles = (klen + MBK - 1) / MBK;
-    const int64_t nfull = klen / MBK;
     if (g.alpha != 0.0f && ntiles > 0) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -349,45 +394,40 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             fb[1][j] = bf16x8_t{};
-        if (nfull > 0)
-            load_tiles_full(kb);
-        else
-            load_tiles_tail(kb);
-        store_tiles(0);
-        __syncthreads();
-        int64_t kt = 0;
-        for (; kt + 1 < nfull; ++kt) {
-            const int st = (int)(kt & 1);
-            load_tiles_full(kb + (kt + 1) * MBK);
-            // keep the next tile's global loads at the top of the iteration
-            // so their latency overlaps this tile's MFMAs
-            __builtin_amdgcn_sched_barrier(0);
-            tile_body(st);
-            store_tiles(st ^ 1);
-            schedule_main_loop();
-            __syncthreads();
+        // prologue: tiles 0 .. D-1
+        for (int64_t v = 0; v < D && v < ntiles; ++v) {
+            if (v == 0 && tail)
+                load_tail(0);
+            else
+                issue_dma(v);
         }
-        for (; kt < ntiles; ++kt) {
-            const int st = (int)(kt & 1);
-            const bool has_next = kt + 1 < ntiles;   // then the next is the partial tile
-            if (has_next)
-                load_tiles_tail(kb + (kt + 1) * MBK);
-            tile_body(st);
-            if (has_next)
-                store_tiles(st ^ 1);
-            __syncthreads();
+        if (tail)
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the register-path LDS writes
+        int64_t v = 0;
+        // steady state: D-1 later tiles stay in flight while tile v is used
+        for (; v + D < ntiles; ++v) {
+            __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm((D - 1) * LPW));
+            barrier();
+            stage_body((int)(v % kStages), true, v + D);
         }
-        mfma_step(fa[1], fb[1]);   // last k step of the last tile
+        // drain
+        for (; v < ntiles; ++v) {
+            __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
+            barrier();
+            stage_body((int)(v % kStages), false, 0);
+        }
+        mfma_step(fa[1], fb[1]);   // k-step 1 of the last stage
+        __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
+        barrier();
     }
 
     // Epilogue, in chunks of EP_ROWS tile rows: every wave writes the
-    // accumulator blocks it owns in the chunk to LDS (the K loop's buffers
-    // are free after its last barrier), then all threads store the chunk
-    // along C's contiguous dimension.  In registers, lane l's value v of a
-    // 32 x 32 block is row 8*(v/4) + 4*(l/32) + v%4, column l%32.
+    // accumulator blocks it owns in the chunk to LDS, then all threads store
+    // the chunk along C's contiguous dimension.  In registers, lane l's value
+    // v of a 32 x 32 block is row 8*(v/4) + 4*(l/32) + v%4, column l%32.
     constexpr int EP_ROWS = 64;
     constexpr int EP_LD = BN + 4;
-    static_assert((EP_ROWS * EP_LD + BN) * 4 <= 2 * (BM + BN) * 8 * 16,
+    static_assert((EP_ROWS * EP_LD + BN) * 4 <= kStages * STAGE_SLOTS * 16,
                   "epilogue chunk and bias fit in LDS");
     float *chunk = (float *)lds;
     // the tile's BN bias values, read from global memory once
@@ -419,21 +459,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
                                                                   bias_s);
         else
             store_chunk<4, false, false, EP_ROWS, BN, EP_LD, NT>(g, tc, chunk, m0, n0, c * EP_ROWS,
-                                                                  bias_s);
+                                                                   bias_s);
         __syncthreads();
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NS>
 hipError_t launch_one(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
-    const size_t lds_bytes = (size_t)2 * (BM + BN) * 8 * sizeof(uint4);
-    auto kern = gemm_mfma_bf16_kernel<BM, BN, WM, WN>;
-    hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds_bytes);
-    if (e != hipSuccess)
-        return e;
+    const size_t lds_bytes = (size_t)NS * (BM + BN) * 4 * sizeof(uint4);
+    auto kern = gemm_mfma_bf16_kernel<BM, BN, WM, WN, NS>;
     hipLaunchKernelGGL(kern, dim3((unsigned)p.programs), dim3(64 * WM * WN), lds_bytes, stream,
                        g);
     return hipGetLastError();
@@ -441,20 +476,24 @@ hipError_t launch_one(const GemmArgs &g, const Plan &p, hipStream_t stream)
 
 } // namespace
 
-// variant index -> instantiation
+// variant index -> instantiation (BM x BN tile, WM x WN wavefronts, ring depth)
 const TileConfig kMfmaBf16Tiles[] = {
-    {256, 256, MBK, 256, 0, "mfma_bf16_256x256x64_w2x2"},
-    {128, 128, MBK, 256, 1, "mfma_bf16_128x128x64_w2x2"},
-    {256, 128, MBK, 256, 2, "mfma_bf16_256x128x64_w2x2"},
+    {256, 256, MBK, 256, 0, "mfma_bf16_256x256x32_w2x2_s4"},
+    {128, 128, MBK, 256, 1, "mfma_bf16_128x128x32_w2x2_s4"},
+    {256, 128, MBK, 256, 2, "mfma_bf16_256x128x32_w2x2_s4"},
+    {256, 128, MBK, 256, 3, "mfma_bf16_256x128x32_w2x2_s3"},
+    {128, 256, MBK, 256, 4, "mfma_bf16_128x256x32_w2x2_s3"},
 };
-const int kNumMfmaBf16Tiles = 3;
+const int kNumMfmaBf16Tiles = 5;
 
 hipError_t launch_mfma_bf16(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
     switch (p.tile.variant) {
-    case 0: return launch_one<256, 256, 2, 2>(g, p, stream);
-    case 1: return launch_one<128, 128, 2, 2>(g, p, stream);
-    case 2: return launch_one<256, 128, 2, 2>(g, p, stream);
+    case 0: return launch_one<256, 256, 2, 2, 4>(g, p, stream);
+    case 1: return launch_one<128, 128, 2, 2, 4>(g, p, stream);
+    case 2: return launch_one<256, 128, 2, 2, 4>(g, p, stream);
+    case 3: return launch_one<256, 128, 2, 2, 3>(g, p, stream);
+    case 4: return launch_one<128, 256, 2, 2, 3>(g, p, stream);
     default: return hipErrorInvalidValue;
     }
 }

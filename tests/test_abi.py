@@ -173,7 +173,7 @@ def test_plans_of_the_five_workloads():
     c3 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c3"]))
     assert "kernel=mfma_bf16" in c3 and "bm=256 bn=256" in c3 and "programs=256" in c3
     c4 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c4"]))
-    assert "kernel=mfma_bf16" in c4
+    assert "kernel=mfma_bf16" in c4 and "bm=128 bn=128" in c4    # 272 tiles of 256^2 quantise badly
     d5 = _desc_for(W.WORKLOADS["c5"])
     ws = dg.dg_gemm_workspace_size(d5)
     assert ws > 0
