@@ -32,6 +32,7 @@ SOURCES = [
     "kernel_generic.hip",
     "kernel_valu_f32.hip",
     "kernel_mfma_bf16.hip",
+    "kernel_mfma_f32.hip",
 ]
 
 

@@ -164,6 +164,13 @@ dg_status validate_ptrs(const dg_gemm_desc *d, const Extents &e, const void *A, 
 
 bool aligned_to(const void *p, int64_t bytes) { return ((uintptr_t)p % bytes) == 0; }
 
+// Batch strides keep every batch entry's A and B 16-byte aligned (they are
+// not used when batch == 1).
+bool strides_aligned(const dg_gemm_desc *d, int64_t elems)
+{
+    return d->batch <= 1 || (d->stride_a % elems == 0 && d->stride_b % elems == 0);
+}
+
 // Eligibility of the specialised kernels.  Pointers may be NULL (query
 // without buffers): they then count as aligned.
 bool valu_eligible(const dg_gemm_desc *d, const void *A, const void *B)
@@ -171,7 +178,7 @@ bool valu_eligible(const dg_gemm_desc *d, const void *A, const void *B)
     if (d->a_type != DG_F32)
         return false;
     return aligned_to(A, 16) && aligned_to(B, 16) && d->lda % 4 == 0 && d->ldb % 4 == 0 &&
-           d->stride_a % 4 == 0 && d->stride_b % 4 == 0;
+           strides_aligned(d, 4);
 }
 
 bool mfma_bf16_eligible(const dg_gemm_desc *d, const void *A, const void *B)
@@ -180,8 +187,7 @@ bool mfma_bf16_eligible(const dg_gemm_desc *d, const void *A, const void *B)
         return false;
     // the kernel addresses a tile with 32-bit byte offsets: 256 rows * ld * 2 < 2^31
     return aligned_to(A, 16) && aligned_to(B, 16) && d->lda % 8 == 0 && d->ldb % 8 == 0 &&
-           d->stride_a % 8 == 0 && d->stride_b % 8 == 0 && d->lda < (1 << 22) &&
-           d->ldb < (1 << 22);
+           strides_aligned(d, 8) && d->lda < (1 << 22) && d->ldb < (1 << 22);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -211,16 +217,21 @@ const TileConfig *forced_tile(const TileConfig *table, int n)
 // tiles = 1.06 waves.  It is used only when the waves it forms are at least
 // 85 % full; otherwise the 128 x 128 tile (two workgroups per CU, 4x the
 // tiles) is used.
-TileConfig pick_mfma_tile(const dg_gemm_desc *d)
+TileConfig pick_quantised(const dg_gemm_desc *d, const TileConfig *table, int n)
 {
-    if (const TileConfig *f = forced_tile(kMfmaBf16Tiles, kNumMfmaBf16Tiles))
+    if (const TileConfig *f = forced_tile(table, n))
         return *f;
-    const TileConfig &t256 = kMfmaBf16Tiles[0], &t128 = kMfmaBf16Tiles[1];
+    const TileConfig &t256 = table[0], &t128 = table[1];
     const int64_t tiles = tiles_of(d, t256);
     const int64_t waves = ceil_div(tiles, kNumCu);
     if (tiles >= kNumCu && tiles * 100 >= waves * kNumCu * 85)
         return t256;
     return t128;
+}
+
+TileConfig pick_mfma_tile(const dg_gemm_desc *d)
+{
+    return pick_quantised(d, kMfmaBf16Tiles, kNumMfmaBf16Tiles);
 }
 
 // Split-K slices for `tiles` output tiles: only when the tiles alone leave
@@ -241,14 +252,18 @@ dg_status make_plan(const dg_gemm_desc *d, const void *A, const void *B, size_t 
 {
     Plan p{};
     const int32_t algo = d->algo;
-    if (algo == DG_ALGO_MFMA_F32)
-        return DG_ERROR_NOT_SUPPORTED;
     if (algo == DG_ALGO_MFMA_BF16 || (algo == DG_ALGO_AUTO && mfma_bf16_eligible(d, A, B))) {
         if (!mfma_bf16_eligible(d, A, B))
             return DG_ERROR_NOT_SUPPORTED;
         p.kernel = KERNEL_MFMA_BF16;
         p.tile = pick_mfma_tile(d);
-    } else if (algo == DG_ALGO_VALU_F32 || (algo == DG_ALGO_AUTO && valu_eligible(d, A, B))) {
+    } else if (algo == DG_ALGO_MFMA_F32 || (algo == DG_ALGO_AUTO && valu_eligible(d, A, B))) {
+        // fp32 on the matrix cores: same operand requirements as the VALU kernel
+        if (!valu_eligible(d, A, B))
+            return DG_ERROR_NOT_SUPPORTED;
+        p.kernel = KERNEL_MFMA_F32;
+        p.tile = pick_quantised(d, kMfmaF32Tiles, kNumMfmaF32Tiles);
+    } else if (algo == DG_ALGO_VALU_F32) {
         if (!valu_eligible(d, A, B))
             return DG_ERROR_NOT_SUPPORTED;
         p.kernel = KERNEL_VALU_F32;
@@ -432,6 +447,7 @@ dg_status dg_gemm(const dg_gemm_desc *d, const void *A, const void *B, void *C, 
     case KERNEL_GENERIC: err = launch_generic(g, p, s); break;
     case KERNEL_VALU_F32: err = launch_valu_f32(g, p, s); break;
     case KERNEL_MFMA_BF16: err = launch_mfma_bf16(g, p, s); break;
+    case KERNEL_MFMA_F32: err = launch_mfma_f32(g, p, s); break;
     default: return DG_ERROR_NOT_SUPPORTED;
     }
     if (err != hipSuccess)

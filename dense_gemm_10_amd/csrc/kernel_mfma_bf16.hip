@@ -45,6 +45,7 @@
 // major); 16-byte aligned base pointers; lda, ldb and the batch strides
 // multiples of 8 elements; BM * lda and BN * ldb small enough for 32-bit
 // byte offsets inside a tile.
+#include "epilogue.hpp"
 #include "launch.hpp"
 
 namespace dg {
@@ -52,7 +53,6 @@ namespace dg {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int MBK = 32;      // K per stage: 4 chunks of 8 bf16 per row
 
@@ -103,116 +103,6 @@ __device__ __forceinline__ uint4 load_chunk_tail(const uint16_t *row, int64_t k_
         w[j / 2] |= (k < ke ? v : 0u) << (16 * (j % 2));
     }
     return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-// Epilogue of one run of VEC consecutive outputs along C's contiguous
-// dimension: v = act(alpha*acc + beta*C + bias).  `go` is the line (row of
-// a row-major C, column of a column-major one), `gi` the first element of
-// the run along the line, `lim` the line length; elements past lim are
-// left untouched.  The branches on beta / bias / act are uniform.
-// Epilogue of one run of VEC consecutive outputs along C's contiguous
-// dimension: v = act(alpha*acc + beta*C + bias).  `go` is the line (row of
-// a row-major C, column of a column-major one), `gi` the first element of
-// the run along the line, `lim` the line length; elements past lim are
-// left untouched.  `bias_run` points at the staged bias of the run's first
-// column.  The branches on beta / bias / act are uniform.
-template <int VEC>
-__device__ __forceinline__ void run_epilogue(const GemmArgs &g, int64_t b, int64_t go, int64_t gi,
-                                             int64_t lim, bool col_major, float (&v)[VEC],
-                                             const float *bias_run)
-{
-#pragma unroll
-    for (int e = 0; e < VEC; ++e)
-        v[e] *= g.alpha;
-    if (g.beta != 0.0f) {
-        const int64_t base = b * g.sc + go * g.ldc + gi;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            if (gi + e < lim)
-                v[e] = fmaf(g.beta, load_as_f32(g.C, g.c_bf16, base + e), v[e]);
-    }
-    if (g.bias) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            v[e] += col_major ? bias_run[0] : bias_run[e];
-    }
-    if (g.act != ACT_NONE) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            v[e] = activate(v[e], g.act);
-    }
-}
-
-// Store rows [r0, r0 + ROWS) of a BM x BN output tile from an LDS chunk
-// (fp32, row-major, row stride LD) to C, or when PARTIAL to the split-K
-// workspace ([split][batch][M][N], row-major).  The NT threads walk C's
-// contiguous dimension in runs of VEC elements (16 bytes: 8 bf16 or 4
-// fp32); a run inside the matrix and 16-byte aligned is written with one
-// vector store, otherwise element by element (ragged edges, odd ldc).
-template <int VEC, bool PARTIAL, bool BF16_OUT, int ROWS, int BN, int LD, int NT>
-__device__ __forceinline__ void store_chunk(const GemmArgs &g, const TileCoord &tc,
-                                            const float *chunk, int64_t m0, int64_t n0, int r0,
-                                            const float *bias_s)
-{
-    const bool col_major = !PARTIAL && g.c_col;
-    const int64_t ld = PARTIAL ? g.N : g.ldc;
-    const int64_t base = PARTIAL ? ((int64_t)tc.s * g.sched.batch + tc.b) * g.M * g.N
-                                 : tc.b * g.sc;
-    // runs per line: along n (row-major) or along m (column-major)
-    const int line_len = col_major ? ROWS : BN;
-    const int runs_per_line = line_len / VEC;
-    const int nruns = ROWS * BN / VEC;
-    const int64_t inner_lim = col_major ? g.M : g.N;
-    const int64_t outer_lim = col_major ? g.N : g.M;
-    for (int r = threadIdx.x; r < nruns; r += NT) {
-        const int line = r / runs_per_line;
-        const int first = (r % runs_per_line) * VEC;
-        // tile-relative coordinates of the run's first element
-        const int row = col_major ? r0 + first : r0 + line;
-        const int col = col_major ? line : first;
-        const int64_t go = col_major ? n0 + col : m0 + row;   // line index in C
-        const int64_t gi = col_major ? m0 + row : n0 + col;   // position along the line
-        if (go >= outer_lim || gi >= inner_lim)
-            continue;
-        float v[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            v[e] = col_major ? chunk[(row - r0 + e) * LD + col] : chunk[(row - r0) * LD + col + e];
-        if (!PARTIAL)
-            run_epilogue<VEC>(g, tc.b, go, gi, inner_lim, col_major, v,
-                              bias_s + col);
-        const int64_t off = base + go * ld + gi;
-        const bool full = gi + VEC <= inner_lim;
-        if (PARTIAL || !BF16_OUT) {
-            float *dst = (PARTIAL ? g.ws : (float *)g.C) + off;
-            if (full && ((uintptr_t)dst & 15) == 0) {
-                *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    if (gi + e < inner_lim)
-                        dst[e] = v[e];
-            }
-        } else {
-            uint16_t *dst = (uint16_t *)g.C + off;
-            uint16_t h[VEC];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                h[e] = f32_to_bf16(v[e]);
-            if (full && ((uintptr_t)dst & 15) == 0) {
-                uint32_t w[VEC / 2];
-#pragma unroll
-                for (int e = 0; e < VEC / 2; ++e)
-                    w[e] = (uint32_t)h[2 * e] | ((uint32_t)h[2 * e + 1] << 16);
-                *(uint4 *)dst = make_uint4(w[0], w[1], w[2], w[3]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    if (gi + e < inner_lim)
-                        dst[e] = h[e];
-            }
-        }
-    }
 }
 
 template <int BM, int BN, int WM, int WN, int kStages>
@@ -421,47 +311,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
         barrier();
     }
 
-    // Epilogue, in chunks of EP_ROWS tile rows: every wave writes the
-    // accumulator blocks it owns in the chunk to LDS, then all threads store
-    // the chunk along C's contiguous dimension.  In registers, lane l's value
-    // v of a 32 x 32 block is row 8*(v/4) + 4*(l/32) + v%4, column l%32.
-    constexpr int EP_ROWS = 64;
-    constexpr int EP_LD = BN + 4;
-    static_assert((EP_ROWS * EP_LD + BN) * 4 <= kStages * STAGE_SLOTS * 16,
+    static_assert(epilogue_lds_bytes(BN) <= kStages * STAGE_SLOTS * 16,
                   "epilogue chunk and bias fit in LDS");
-    float *chunk = (float *)lds;
-    // the tile's BN bias values, read from global memory once
-    float *bias_s = chunk + EP_ROWS * EP_LD;
-    if (g.bias && !g.write_partial) {
-        for (int t = tid; t < BN; t += NT)
-            bias_s[t] = n0 + t < N ? load_as_f32(g.bias, g.bias_bf16, n0 + t) : 0.0f;
-    }
-#pragma unroll
-    for (int c = 0; c < BM / EP_ROWS; ++c) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int row0 = wm * TM + i * 32 - c * EP_ROWS;   // block's first row in the chunk
-            if (row0 >= 0 && row0 < EP_ROWS) {
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        chunk[(row0 + 8 * (v / 4) + 4 * frag_half + (v % 4)) * EP_LD + wn * TN +
-                              j * 32 + (lane & 31)] = acc[i][j][v];
-            }
-        }
-        __syncthreads();
-        if (g.write_partial)
-            store_chunk<4, true, false, EP_ROWS, BN, EP_LD, NT>(g, tc, chunk, m0, n0, c * EP_ROWS,
-                                                                  bias_s);
-        else if (g.c_bf16)
-            store_chunk<8, false, true, EP_ROWS, BN, EP_LD, NT>(g, tc, chunk, m0, n0, c * EP_ROWS,
-                                                                  bias_s);
-        else
-            store_chunk<4, false, false, EP_ROWS, BN, EP_LD, NT>(g, tc, chunk, m0, n0, c * EP_ROWS,
-                                                                   bias_s);
-        __syncthreads();
-    }
+    tile_epilogue<BM, BN, WM, WN>(g, tc, (float *)lds, m0, n0, acc);
 }
 
 template <int BM, int BN, int WM, int WN, int NS>

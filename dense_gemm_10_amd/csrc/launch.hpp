@@ -37,12 +37,14 @@ struct Plan {
 hipError_t launch_generic(const GemmArgs &g, const Plan &p, hipStream_t stream);
 hipError_t launch_valu_f32(const GemmArgs &g, const Plan &p, hipStream_t stream);
 hipError_t launch_mfma_bf16(const GemmArgs &g, const Plan &p, hipStream_t stream);
+hipError_t launch_mfma_f32(const GemmArgs &g, const Plan &p, hipStream_t stream);
 hipError_t launch_splitk_reduce(const GemmArgs &g, const Plan &p, hipStream_t stream);
 
 // Tile configurations of each family (defined next to the kernels).
 extern const TileConfig kGenericTiles[];
 extern const TileConfig kValuTiles[];
 extern const TileConfig kMfmaBf16Tiles[];
-extern const int kNumGenericTiles, kNumValuTiles, kNumMfmaBf16Tiles;
+extern const TileConfig kMfmaF32Tiles[];
+extern const int kNumGenericTiles, kNumValuTiles, kNumMfmaBf16Tiles, kNumMfmaF32Tiles;
 
 } // namespace dg

@@ -70,7 +70,12 @@ typedef enum { DG_ACT_NONE = 0, DG_ACT_GELU_ERF = 1, DG_ACT_GELU_TANH = 2 } dg_a
 
 /* Kernel family selection (benchmarking and ablation; 0 lets the library
  * choose).  GENERIC is the plain LDS-tiled kernel that serves every
- * layout, alignment and dtype. */
+ * layout, alignment and dtype.  For fp32 the automatic choice is the
+ * matrix-core kernel (MFMA_F32) when the operands are 16-byte aligned with
+ * leading dimensions and batch strides multiple of 4; VALU_F32 (the
+ * register-tiled vector-FMA kernel) takes the same operands and is used
+ * only when asked for.  Forcing a family whose requirements the operands
+ * do not meet returns DG_ERROR_NOT_SUPPORTED. */
 typedef enum {
     DG_ALGO_AUTO = 0,
     DG_ALGO_GENERIC = 1,

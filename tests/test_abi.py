@@ -167,9 +167,11 @@ def _desc_for(p, **kw):
 
 def test_plans_of_the_five_workloads():
     c1 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c1"]))
-    assert "kernel=valu_f32" in c1 and "splits=1" in c1
+    assert "kernel=mfma_f32" in c1 and "splits=1" in c1 and "bm=128" in c1
     c2 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c2"]))
-    assert "kernel=valu_f32" in c2 and "programs=1024" in c2
+    assert "kernel=mfma_f32" in c2 and "programs=256" in c2
+    c2v = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c2"], algo=dg.DG_ALGO_VALU_F32))
+    assert "kernel=valu_f32" in c2v and "programs=1024" in c2v
     c3 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c3"]))
     assert "kernel=mfma_bf16" in c3 and "bm=256 bn=256" in c3 and "programs=256" in c3
     c4 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c4"]))
@@ -189,9 +191,22 @@ def test_layouts_outside_the_fast_paths_use_the_generic_kernel():
         _desc(a_type="bf16", a_order="col"))                          # bf16 A not K-contiguous
     d = _desc(a_type="bf16", b_order="col", lda=36)                    # lda not a multiple of 8
     assert "kernel=generic" in dg.dg_gemm_describe(d)
-    with pytest.raises(dg.DgError) as e:
-        dg.dg_gemm_describe(_desc(a_type="bf16", algo=dg.DG_ALGO_MFMA_BF16))
-    assert e.value.status == dg.DG_ERROR_NOT_SUPPORTED
+    for bad in [_desc(a_type="bf16", algo=dg.DG_ALGO_MFMA_BF16),      # B not column-major
+                _desc(lda=33, algo=dg.DG_ALGO_MFMA_F32),                  # ld not a multiple of 4
+                _desc(lda=33, algo=dg.DG_ALGO_VALU_F32),
+                _desc(a_type="bf16", b_order="col", algo=dg.DG_ALGO_VALU_F32)]:
+        with pytest.raises(dg.DgError) as e:
+            dg.dg_gemm_describe(bad)
+        assert e.value.status == dg.DG_ERROR_NOT_SUPPORTED
+
+
+def test_batch_strides_ignored_for_a_single_matrix():
+    # odd strides do not matter when batch == 1 ...
+    d = _desc(M=64, N=48, K=32, stride_a=12345, stride_b=777)
+    assert "kernel=mfma_f32" in dg.dg_gemm_describe(d)
+    # ... but do when there is a batch
+    d = _desc(M=64, N=48, K=32, batch=2, stride_a=12345, stride_b=777 * 4)
+    assert "kernel=generic" in dg.dg_gemm_describe(d)
 
 
 def test_k_zero_and_alpha_zero_never_split():

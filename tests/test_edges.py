@@ -60,7 +60,11 @@ def _make_cases(n, seed):
                       lda=_ld(ao, M, K, pad), ldb=_ld(bo, K, N, pad), ldc=_ld(co, M, N, pad),
                       alpha=alpha, beta=beta, has_bias=has_bias, bias_type=ta, act=act,
                       split_k=split, seed=1000 + i, **kw)
-        cases.append((p, ALGOS[i % 4]))
+        algo = ALGOS[i % 4]
+        if (ta == W.F32 and i % 4 == 2 and p.lda_ % 4 == 0 and p.ldb_ % 4 == 0 and
+                p.stride_a_ % 4 == 0 and p.stride_b_ % 4 == 0):
+            algo = dg.DG_ALGO_VALU_F32        # the vector-FMA kernel, where it applies
+        cases.append((p, algo))
     return cases
 
 

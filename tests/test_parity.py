@@ -58,6 +58,12 @@ def test_c1_sgemm_256(small_int):
     _full(W.WORKLOADS["c1"], small_int)
 
 
+@pytest.mark.parametrize("small_int", [False, True])
+def test_c1_sgemm_256_valu(small_int):
+    import dense_gemm_10_amd as dg
+    _full(W.WORKLOADS["c1"], small_int, algo=dg.DG_ALGO_VALU_F32)
+
+
 # --- C2: fp32 4096^3 -----------------------------------------------------------
 def test_c2_sgemm_4096_sampled():
     _sampled(W.WORKLOADS["c2"])
@@ -67,10 +73,19 @@ def test_c2_sgemm_4096_sampled_int():
     _sampled(W.WORKLOADS["c2"], n=1000, small_int=True)
 
 
+def test_c2_sgemm_4096_sampled_valu():
+    import dense_gemm_10_amd as dg
+    _sampled(W.WORKLOADS["c2"], algo=dg.DG_ALGO_VALU_F32)
+
+
 @pytest.mark.parametrize("small_int", [False, True])
-def test_c2_reduced_twin_ragged(small_int):
-    p = W.WORKLOADS["c2"].replace(name="sgemm_f32_ragged", M=515, N=389, K=301)
-    _full(p, small_int)
+@pytest.mark.parametrize("algo", [0, 2])        # automatic (matrix cores), vector FMA
+def test_c2_reduced_twin_ragged(small_int, algo):
+    # ragged sizes, leading dimensions padded to multiples of 4 (both fp32
+    # kernels need 16-byte rows)
+    p = W.WORKLOADS["c2"].replace(name="sgemm_f32_ragged", M=515, N=389, K=301,
+                                  lda=304, ldb=392, ldc=396)
+    _full(p, small_int, algo=algo)
 
 
 # --- C3: bf16 4096^3, A row, B col, bf16 out -------------------------------------
