@@ -108,6 +108,148 @@ def time_copy(steps, warmup, nbytes=512 << 20):
             "gbps_read_plus_write": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    """Hash of every HIP / C++ source of the library: a profile taken with a
+    different hash describes other kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_gemm_10_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _rocprof(args, outdir, timeout_s=150):
+    """Run rocprofv3 (killed after timeout_s) on a child bench.py; returns
+    the CSV rows of the first *<suffix>.csv it produced."""
+    import shutil
+    import subprocess
+    shutil.rmtree(outdir, ignore_errors=True)
+    cmd = ["timeout", "-s", "KILL", str(timeout_s), "rocprofv3"] + args + [
+        "-f", "csv", "-d", outdir, "-o", "run", "--", sys.executable, os.path.abspath(__file__)]
+    return cmd
+
+
+def _csv_rows(outdir, suffix):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(outdir, "**", "*" + suffix), recursive=True)
+    if not files:
+        raise RuntimeError(f"rocprofv3 wrote no *{suffix} under {outdir}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _per_dispatch(rows, name_filter):
+    """Mean over dispatches of the per-dispatch sum (over instances) of the
+    counter, for kernels whose name contains name_filter."""
+    import collections
+    per = collections.defaultdict(float)
+    for r in rows:
+        if name_filter in r["Kernel_Name"]:
+            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not per:
+        raise RuntimeError(f"no dispatch of a kernel matching {name_filter!r}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def _shown(cmd, tmp):
+    """A recorded command as it reads from the repository root: the
+    interpreter as python3, this file as bench.py, temp output as $OUT."""
+    text = " ".join(cmd).replace(sys.executable, "python3")
+    text = text.replace(os.path.join(ROOT, "bench.py"), "bench.py")
+    return text.replace(tmp, "$OUT")
+
+
+def collect_profile(workload, tmp, out_dir=PROFILES):
+    """Kernel-trace statistics and HBM traffic counters of one workload,
+    written to profiles/.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+    are each scaled by the ratio between the bytes a plain device copy of
+    known size moves and what the same counter reports for it."""
+    import subprocess
+    child = ["--workload", workload, "--secondary", "none", "--no-cpu-baseline"]
+    results = {}
+    # 1. kernel trace with statistics
+    out = os.path.join(tmp, "trace")
+    cmd = _rocprof(["--kernel-trace", "--stats"], out) + child + ["--steps", "20", "--warmup", "5"]
+    log(f"[profile] {' '.join(cmd)}")
+    subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL)
+    stats = _csv_rows(out, "kernel_stats.csv")
+    results["trace_command"] = _shown(cmd, tmp)
+    results["kernel_stats"] = [{k: r[k] for k in ("Name", "Calls", "AverageNs", "MinNs", "MaxNs",
+                                                 "Percentage")} for r in stats]
+    # 2. traffic counters, GEMM and copy calibration
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        out = os.path.join(tmp, counter)
+        cmd = _rocprof(["--pmc", counter], out) + child + ["--steps", "3", "--warmup", "1"]
+        log(f"[profile] {' '.join(cmd)}")
+        subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL)
+        kib, n = _per_dispatch(_csv_rows(out, "counter_collection.csv"), "gemm_")
+        out_c = os.path.join(tmp, counter + "_copy")
+        cmd_c = _rocprof(["--pmc", counter], out_c) + ["--workload", "copy", "--steps", "3",
+                                                        "--warmup", "1"]
+        subprocess.run(cmd_c, check=True, stdout=subprocess.DEVNULL)
+        copy_kib, _ = _per_dispatch(_csv_rows(out_c, "counter_collection.csv"), "copy")
+        scale = (512 << 20) / (copy_kib * 1024.0)
+        results[counter] = {"kib_per_dispatch": kib, "dispatches": n,
+                            "copy_kib_per_dispatch": copy_kib, "copy_bytes": 512 << 20,
+                            "scale": scale, "bytes_per_dispatch": kib * 1024.0 * scale,
+                            "command": _shown(cmd, tmp), "copy_command": _shown(cmd_c, tmp)}
+    results["kernel_source_hash"] = kernel_source_hash()
+    results["workload"] = workload
+    write_profile(results, out_dir)
+    return results
+
+
+def write_profile(results, out_dir=PROFILES):
+    """Write traffic_<workload>.json and a markdown summary of `results`."""
+    workload = results["workload"]
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"traffic_{workload}.json"), "w") as f:
+        json.dump(results, f, indent=1)
+    import workloads as W
+    p = W.WORKLOADS[workload]
+    lines = [f"# rocprofv3 summary: {p.name}", "",
+             f"Made by `python3 bench.py --workload {workload} --collect-profile` from the "
+             "repository root, which runs the commands below ($OUT is a temporary folder).", "",
+             f"Kernel sources hash: `{results['kernel_source_hash']}`", "",
+             "## Kernel trace statistics", "", f"Command: `{results['trace_command']}`", "",
+             "| kernel | calls | average ns | min ns | max ns | % |", "|---|---|---|---|---|---|"]
+    for r in results["kernel_stats"]:
+        lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    lines += ["", "## HBM traffic per GEMM dispatch", "",
+              "| counter | KiB / dispatch | copy calibration KiB (512 MiB copy) | scale | bytes |",
+              "|---|---|---|---|---|"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        t = results[c]
+        lines.append(f"| {c} | {t['kib_per_dispatch']:.0f} | {t['copy_kib_per_dispatch']:.0f} | "
+                     f"{t['scale']:.3f} | {t['bytes_per_dispatch']:.4g} |")
+    lines += ["", f"Commands: `{results['FETCH_SIZE']['command']}`, "
+              f"`{results['WRITE_SIZE']['command']}`; calibration: "
+              f"`{results['FETCH_SIZE']['copy_command']}`", ""]
+    with open(os.path.join(out_dir, f"{workload}_{p.name}.md"), "w") as f:
+        f.write("\n".join(lines))
+
+
+def traffic_for(workload):
+    """HBM bytes per launch from profiles/, or None when missing or taken
+    with other kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t["FETCH_SIZE"]["bytes_per_dispatch"] + t["WRITE_SIZE"]["bytes_per_dispatch"]
+
+
 def cpu_baseline(name, budget_s=12.0):
     """Oracle throughput on a seeded sample of the workload's outputs."""
     import numpy as np
@@ -145,7 +287,21 @@ def main():
     ap.add_argument("--algo", type=int, default=0)
     ap.add_argument("--group-m", type=int, default=0)
     ap.add_argument("--xcd-remap", type=int, default=0)
+    ap.add_argument("--collect-profile", action="store_true",
+                    help="run rocprofv3 (kernel trace, FETCH_SIZE, WRITE_SIZE) on this workload "
+                         "and write profiles/traffic_<workload>.json")
+    ap.add_argument("--profile-dir", default=PROFILES,
+                    help="where --collect-profile writes (default: profiles/)")
     args = ap.parse_args()
+
+    if args.collect_profile:
+        import tempfile
+        with tempfile.TemporaryDirectory(dir=os.environ.get("TMPDIR", "/tmp")) as tmp:
+            r = collect_profile(args.workload, tmp, args.profile_dir)
+        print(json.dumps({"workload": args.workload,
+                          "fetch_bytes": r["FETCH_SIZE"]["bytes_per_dispatch"],
+                          "write_bytes": r["WRITE_SIZE"]["bytes_per_dispatch"]}), flush=True)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -177,6 +333,8 @@ def main():
         achieved = p.flops() / (main_r["ms"] * 1e-3)
         roof = {"bound": bound, "achieved": achieved / 1e12, "peak": peak / 1e12,
                 "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None}
+    traffic = traffic_for(args.workload)
+    roof["traffic"] = traffic
     roof["kernel"] = main_r["kernel"]
     roof["algorithmic_bytes"] = acc.problem_bytes(p)
     roof["algorithmic_flops"] = p.flops()
