@@ -27,6 +27,9 @@ struct GemmArgs {
     int32_t act;                   // dg_act
     int32_t write_partial;         // 1: store raw fp32 partials to ws, no epilogue
     int32_t ab_bf16;               // input dtype of A and B: 1 = bf16, 0 = fp32
+    int32_t out_vec16;             // 1: the output (C, or ws when write_partial) is
+                                   // row-major and every row of every batch entry
+                                   // starts on a 16-byte boundary
     SchedArgs sched;
 };
 

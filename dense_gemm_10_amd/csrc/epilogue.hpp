@@ -11,6 +11,18 @@ namespace dg {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// accesses, not for its global stores.  __syncthreads() also waits for every
+// outstanding global store (its release fence covers global memory), which
+// would serialise the chunks of the epilogue on HBM write latency; the
+// stores read their data from registers at issue, so nothing here needs
+// them to have landed.  The memory clobber keeps the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Epilogue of one run of VEC consecutive outputs along C's contiguous
 // dimension: v = act(alpha*acc + beta*C + bias).  `go` is the line (row of
 // a row-major C, column of a column-major one), `gi` the first element of
@@ -121,28 +133,154 @@ __device__ __forceinline__ void store_chunk(const GemmArgs &g, const TileCoord &
     }
 }
 
-// LDS bytes tile_epilogue needs for a tile BN columns wide.
+// LDS bytes tile_epilogue needs for a tile BN columns wide.  A staged row
+// is BN + 8 floats: the two 32-lane halves of a wave's accumulator write,
+// 4 rows apart, then fall on disjoint halves of the 64 banks, and rows stay
+// 16-byte aligned.
 constexpr int kEpilogueRows = 64;
-constexpr int epilogue_lds_bytes(int BN) { return (kEpilogueRows * (BN + 4) + BN) * 4; }
+constexpr int epilogue_ld(int BN) { return BN + 8; }
+constexpr int epilogue_lds_bytes(int BN) { return (kEpilogueRows * epilogue_ld(BN) + BN) * 4; }
+
+// Accumulator blocks of rows [c * EP_ROWS, (c + 1) * EP_ROWS) of the tile into
+// the LDS chunk (fp32, row stride EP_LD).  Lane l's value v of a 32 x 32
+// block is row 8*(v/4) + 4*(l/32) + v%4, column l%32 of that block; wave
+// (wm, wn) owns blocks FM x FN at rows wm*TM + 32i, columns wn*TN + 32j.
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void stage_chunk(float *chunk, int c,
+                                            const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
+{
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int EP_ROWS = kEpilogueRows, EP_LD = epilogue_ld(BN);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int frag_half = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int row0 = wm * TM + i * 32 - c * EP_ROWS;   // block's first row in the chunk
+        if (row0 >= 0 && row0 < EP_ROWS) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    chunk[(row0 + 8 * (v / 4) + 4 * frag_half + (v % 4)) * EP_LD + wn * TN + j * 32 +
+                          (lane & 31)] = acc[i][j][v];
+        }
+    }
+}
+
+// Epilogue of a tile that lies entirely inside the output, when every
+// output row starts on a 16-byte boundary (out_vec16): each thread turns
+// 16-byte runs of the staged chunk into one 16-byte store (8 bf16 or 4
+// fp32), with 32-bit offsets inside the tile and no per-element masks.
+// PARTIAL writes raw fp32 partials to the split-K workspace instead.
+template <int BM, int BN, int WM, int WN, bool PARTIAL, bool BF16_OUT>
+__device__ __forceinline__ void tile_epilogue_fast(const GemmArgs &g, const TileCoord &tc,
+                                                   float *lds, int64_t m0, int64_t n0,
+                                                   const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
+{
+    constexpr int NT = 64 * WM * WN;
+    constexpr int EP_ROWS = kEpilogueRows, EP_LD = epilogue_ld(BN);
+    constexpr int VEC = BF16_OUT ? 8 : 4;             // outputs per 16-byte store
+    constexpr int RUNS_PER_ROW = BN / VEC;
+    constexpr int RUNS = EP_ROWS * RUNS_PER_ROW;
+    static_assert(RUNS % NT == 0, "whole runs per thread");
+    constexpr int ES = BF16_OUT ? 2 : 4;              // output element size
+    const int tid = threadIdx.x;
+    float *chunk = lds;
+    float *bias_s = chunk + EP_ROWS * EP_LD;
+    char *out;
+    int64_t ld_bytes;
+    if (PARTIAL) {
+        out = (char *)(g.ws + ((int64_t)tc.s * g.sched.batch + tc.b) * g.M * g.N + m0 * g.N + n0);
+        ld_bytes = g.N * 4;
+    } else {
+        out = (char *)g.C + (tc.b * g.sc + m0 * g.ldc + n0) * ES;
+        ld_bytes = g.ldc * ES;
+    }
+    const bool has_bias = !PARTIAL && g.bias;
+    if (has_bias) {
+        for (int t = tid; t < BN; t += NT)
+            bias_s[t] = load_as_f32(g.bias, g.bias_bf16, n0 + t);
+    }
+#pragma unroll
+    for (int c = 0; c < BM / EP_ROWS; ++c) {
+        stage_chunk<BM, BN, WM, WN>(chunk, c, acc);
+        lds_barrier();
+#pragma unroll
+        for (int k = 0; k < RUNS / NT; ++k) {
+            const int r = tid + k * NT;
+            const int row = r / RUNS_PER_ROW;
+            const int col = (r % RUNS_PER_ROW) * VEC;
+            float v[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4) {
+                const float4 q = *(const float4 *)&chunk[row * EP_LD + col + e];
+                v[e] = q.x; v[e + 1] = q.y; v[e + 2] = q.z; v[e + 3] = q.w;
+            }
+            char *dst = out + (int64_t)(c * EP_ROWS + row) * ld_bytes + col * ES;
+            if (!PARTIAL) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    v[e] *= g.alpha;
+                if (g.beta != 0.0f) {
+                    const uint4 cin = *(const uint4 *)dst;
+                    const uint32_t w[4] = {cin.x, cin.y, cin.z, cin.w};
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        const float x = BF16_OUT ? bf16_to_f32((uint16_t)(w[e / 2] >> (16 * (e % 2))))
+                                                 : __uint_as_float(w[e]);
+                        v[e] = fmaf(g.beta, x, v[e]);
+                    }
+                }
+                if (has_bias) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        v[e] += bias_s[col + e];
+                }
+                if (g.act != ACT_NONE) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        v[e] = activate(v[e], g.act);
+                }
+            }
+            if (BF16_OUT) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = (uint32_t)f32_to_bf16(v[2 * e]) | ((uint32_t)f32_to_bf16(v[2 * e + 1]) << 16);
+                *(uint4 *)dst = make_uint4(w[0], w[1], w[2], w[3]);
+            } else {
+                *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+        lds_barrier();
+    }
+}
 
 // Stage and store the whole tile.  `lds` must hold epilogue_lds_bytes(BN)
-// bytes and no wave may still be reading it for other purposes.  In
-// registers, lane l's value v of a 32 x 32 block is row 8*(v/4) + 4*(l/32)
-// + v%4, column l%32 of that block; wave (wm, wn) owns blocks FM x FN at
-// rows wm*TM + 32i, columns wn*TN + 32j.
+// bytes and no wave may still be reading it for other purposes.  Tiles
+// inside the output with 16-byte aligned rows take tile_epilogue_fast; the
+// rest (ragged edges, column-major C, unaligned rows) go through the
+// masked, element-wise store_chunk.
 template <int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs &g, const TileCoord &tc, float *lds,
                                               int64_t m0, int64_t n0,
                                               const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
 {
+    if (g.out_vec16 && m0 + BM <= g.M && n0 + BN <= g.N) {
+        if (g.write_partial)
+            tile_epilogue_fast<BM, BN, WM, WN, true, false>(g, tc, lds, m0, n0, acc);
+        else if (g.c_bf16)
+            tile_epilogue_fast<BM, BN, WM, WN, false, true>(g, tc, lds, m0, n0, acc);
+        else
+            tile_epilogue_fast<BM, BN, WM, WN, false, false>(g, tc, lds, m0, n0, acc);
+        return;
+    }
     constexpr int NT = 64 * WM * WN;
-    constexpr int TM = BM / WM, TN = BN / WN;
-    constexpr int FM = TM / 32, FN = TN / 32;
     constexpr int EP_ROWS = kEpilogueRows;
-    constexpr int EP_LD = BN + 4;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    const int frag_half = lane >> 5;
+    constexpr int EP_LD = epilogue_ld(BN);
+    const int tid = threadIdx.x;
     float *chunk = lds;
     // the tile's BN bias values, read from global memory once
     float *bias_s = chunk + EP_ROWS * EP_LD;
@@ -152,19 +290,8 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs &g, const TileCoord
     }
 #pragma unroll
     for (int c = 0; c < BM / EP_ROWS; ++c) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int row0 = wm * TM + i * 32 - c * EP_ROWS;   // block's first row in the chunk
-            if (row0 >= 0 && row0 < EP_ROWS) {
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        chunk[(row0 + 8 * (v / 4) + 4 * frag_half + (v % 4)) * EP_LD + wn * TN +
-                              j * 32 + (lane & 31)] = acc[i][j][v];
-            }
-        }
-        __syncthreads();
+        stage_chunk<BM, BN, WM, WN>(chunk, c, acc);
+        lds_barrier();
         if (g.write_partial)
             store_chunk<4, true, false, EP_ROWS, BN, EP_LD, NT>(g, tc, chunk, m0, n0, c * EP_ROWS,
                                                                   bias_s);
@@ -174,7 +301,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs &g, const TileCoord
         else
             store_chunk<4, false, false, EP_ROWS, BN, EP_LD, NT>(g, tc, chunk, m0, n0, c * EP_ROWS,
                                                                    bias_s);
-        __syncthreads();
+        lds_barrier();
     }
 }
 

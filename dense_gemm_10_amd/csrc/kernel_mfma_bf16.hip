@@ -16,18 +16,22 @@
 // Data path:
 //   global -> LDS: direct DMA (global_load_lds_dwordx4): each instruction
 //     moves 64 x 16 bytes, lane l's 16 bytes landing at LDS address
-//     M0 + 16 l, without passing through registers.  A K tile (BK = 32) of
-//     A and of B is a "stage"; NSTAGE stages form a ring and the loads of
-//     tile t + NSTAGE - 1 are issued while tile t is multiplied, so each
-//     load has NSTAGE - 1 tiles of MFMA work to arrive in.
-//   LDS layout: a stage row (one row of A, or one column of B) is 64 bytes
-//     = 4 chunks of 8 bf16; logical chunk c of row r is stored at slot
-//     c ^ ((r / 4) mod 4).  The LDS serves a 128-bit access 16 lanes at a
-//     time over 256 bytes of banks; 16 lanes reading one logical chunk of
-//     16 consecutive rows then hit 16 different 16-byte bank groups.  The
-//     DMA lanes are assigned so that consecutive lanes fill consecutive
-//     slots: lane l loads the global chunk that belongs in slot l.
-//   LDS -> registers: ds_read_b128 fragments, 2 k-steps of 16 per stage;
+//     M0 + 16 l, without passing through registers.  A K tile (BK = 32 or
+//     64) of A and of B is a "stage"; NSTAGE stages form a ring and the
+//     loads of tile t + NSTAGE - 1 are issued while tile t is multiplied, so
+//     each load has NSTAGE - 1 tiles of MFMA work to arrive in.  With
+//     BK = 64 a row of a stage is a whole 128-byte line of A or B; 64-byte
+//     half lines were measured to cap the L2 -> CU stream at about 80 % of
+//     what whole lines reach.
+//   LDS layout: a stage row (one row of A, or one column of B) is BK * 2
+//     bytes = CPR chunks of 8 bf16; logical chunk c of row r is stored at
+//     slot c ^ ((r / (16 / CPR)) mod CPR).  The LDS serves a 128-bit access
+//     16 lanes at a time over 256 bytes of banks; 16 lanes reading one
+//     logical chunk of 16 consecutive rows then hit 16 different 16-byte
+//     bank groups.  The DMA lanes are assigned so that consecutive lanes
+//     fill consecutive slots: lane l loads the global chunk that belongs in
+//     slot l.
+//   LDS -> registers: ds_read_b128 fragments, BK / 16 k-steps per stage;
 //   MFMA: each wavefront owns a TM x TN wave tile = FM x FN blocks of
 //     32 x 32, accumulated in FM*FN*16 fp32 registers per lane.
 // The DMA is issued through inline assembly so that the compiler does not
@@ -54,7 +58,6 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int MBK = 32;      // K per stage: 4 chunks of 8 bf16 per row
 
 // s_waitcnt immediate: wait until at most n vector-memory loads of this
 // wave are outstanding and all its LDS operations have completed (expcnt
@@ -105,20 +108,34 @@ __device__ __forceinline__ uint4 load_chunk_tail(const uint16_t *row, int64_t k_
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-template <int BM, int BN, int WM, int WN, int kStages>
+// Swizzle key of stage row r for CPR 16-byte chunks per row: rows that
+// share a 256-byte bank line get different keys, and so do the 16 rows one
+// 16-lane group of a fragment read touches.
+template <int CPR>
+__device__ __forceinline__ int swizzle_key(int r)
+{
+    return (r / (16 / CPR)) % CPR;
+}
+
+template <int BM, int BN, int WM, int WN, int kStages, int MBK>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g)
 {
     constexpr int NT = 64 * WM * WN;
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;    // wave tile
     constexpr int FM = TM / 32, FN = TN / 32;    // 32x32 blocks per wave
+    constexpr int CPR = MBK / 8;                 // 16-byte chunks per stage row
+    constexpr int KS = MBK / 16;                 // MFMA k-steps per stage
+    constexpr int RPI = 64 / CPR;                // stage rows per DMA instruction
     constexpr int ROWS = BM + BN;                // stage rows: A rows, then B columns
-    constexpr int GROUPS = ROWS / 16;            // DMA instructions (16 rows each) per stage
+    constexpr int GROUPS = ROWS / RPI;           // DMA instructions per stage
     constexpr int LPW = GROUPS / NW;             // ... per wave
-    constexpr int STAGE_SLOTS = ROWS * 4;        // 16-byte slots per stage
+    constexpr int STAGE_SLOTS = ROWS * CPR;      // 16-byte slots per stage
     constexpr int D = kStages - 1;               // prefetch distance (tiles)
+    static_assert(MBK == 32 || MBK == 64, "stage K width");
+    static_assert(KS % 2 == 0, "fragment sets alternate per k-step");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
-    static_assert(BM % 16 == 0 && BN % 16 == 0 && GROUPS % NW == 0, "DMA split");
+    static_assert(BM % RPI == 0 && BN % RPI == 0 && GROUPS % NW == 0, "DMA split");
 
     extern __shared__ uint4 lds[];
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)lds;
@@ -142,18 +159,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
     const uint16_t *B_tile = (const uint16_t *)g.B + tc.b * g.sb + n0 * ldb;
 
     // This lane's DMA sources: group q = wave * LPW + i covers stage rows
-    // 16q .. 16q+15 (A rows first, then B columns); lane l fills slot
-    // 64q + l = (row 16q + l/4, physical chunk l%4), i.e. logical chunk
-    // (l%4) ^ ((row/4)%4).  Byte offsets are relative to the tile's first
-    // row and K position; rows past the matrix are clamped.
+    // RPI q .. RPI q + RPI - 1 (A rows first, then B columns); lane l fills
+    // slot 64q + l = (row RPI q + l / CPR, physical chunk l % CPR), i.e.
+    // logical chunk (l % CPR) ^ key(row).  Byte offsets are relative to the
+    // tile's first row and K position; rows past the matrix are clamped.
     uint32_t voff[LPW];
     bool from_a[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int q = wave * LPW + i;
-        const int srow = q * 16 + lane / 4;           // stage row
-        const int c = (lane & 3) ^ ((srow >> 2) & 3); // logical chunk
-        from_a[i] = q * 16 < BM;                      // per group, hence wave-uniform
+        const int srow = q * RPI + lane / CPR;                     // stage row
+        const int c = (lane % CPR) ^ swizzle_key<CPR>(srow);       // logical chunk
+        from_a[i] = q * RPI < BM;                     // per group, hence wave-uniform
         int64_t r = from_a[i] ? srow : srow - BM;     // row inside the A / B tile
         const int64_t lim = from_a[i] ? M - m0 : N - n0;
         r = r < lim ? r : lim - 1;
@@ -193,8 +210,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             const int q = wave * LPW + i;
-            const int srow = q * 16 + lane / 4;
-            const int c = (lane & 3) ^ ((srow >> 2) & 3);
+            const int srow = q * RPI + lane / CPR;
+            const int c = (lane % CPR) ^ swizzle_key<CPR>(srow);
             const uint16_t *rowp = (const uint16_t *)((const char *)(from_a[i] ? A_tile : B_tile) +
                                                       voff[i]) - c * 8;
             stage[q * 64 + lane] = load_chunk_tail(rowp, k0 + c * 8, ke);
@@ -212,19 +229,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
 
     const int frag_row = lane & 31;       // row of A / column of B this lane feeds
     const int frag_half = lane >> 5;      // which 8 of the 16 k of one MFMA step
-    const int swz = (frag_row >> 2) & 3;  // swizzle key (wave tiles are 32-aligned)
+    const int swz = swizzle_key<CPR>(frag_row);   // key of every fragment row (period 16)
 
-    // Fragments of k-step ks (0 or 1) of a stage.
+    // Fragments of k-step ks (0 .. KS-1) of a stage.
     auto load_frags = [&](int st, int ks, bf16x8_t *af, bf16x8_t *bf) {
-        const uint4 *as = lds + st * STAGE_SLOTS + (wm * TM + frag_row) * 4;
-        const uint4 *bs = lds + st * STAGE_SLOTS + (BM + wn * TN + frag_row) * 4;
+        const uint4 *as = lds + st * STAGE_SLOTS + (wm * TM + frag_row) * CPR;
+        const uint4 *bs = lds + st * STAGE_SLOTS + (BM + wn * TN + frag_row) * CPR;
         const int c = (ks * 2 + frag_half) ^ swz;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            af[i] = __builtin_bit_cast(bf16x8_t, as[i * 32 * 4 + c]);
+            af[i] = __builtin_bit_cast(bf16x8_t, as[i * 32 * CPR + c]);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            bf[j] = __builtin_bit_cast(bf16x8_t, bs[j * 32 * 4 + c]);
+            bf[j] = __builtin_bit_cast(bf16x8_t, bs[j * 32 * CPR + c]);
     };
 
     auto mfma_step = [&](const bf16x8_t *af, const bf16x8_t *bf) {
@@ -235,36 +252,48 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     };
 
-    // Two fragment register sets; fa[1]/fb[1] carry k-step 1 of a stage
-    // into the next iteration, whose MFMAs run after the barrier while the
-    // new stage's first fragments are being read.
+    // Two fragment register sets, alternating per k-step; fa[1]/fb[1]
+    // carry the last k-step of a stage into the next iteration, whose MFMAs
+    // run after the barrier while the new stage's first fragments are read.
     bf16x8_t fa[2][FM], fb[2][FN];
 
-    // One stage: k-step 0's fragments are read first, then (in the steady
-    // state) the DMA of a later tile is issued, then the deferred MFMAs run
-    // while those reads land, then k-step 1's fragments are read while
-    // k-step 0's MFMAs run.
-    // The DMA instructions are spread over the deferred MFMAs (one after
-    // every MFMA_PER_DMA of them): a burst of DMA issues can stall the wave
-    // on a full memory queue while the matrix pipe runs dry.
-    constexpr int MFMA_PER_DMA = (FM * FN) / LPW > 0 ? (FM * FN) / LPW : 1;
+    // One stage, as KS k-steps of FM * FN fenced slots.  Slot n of k-step ks
+    // issues the MFMA of block n on the previous k-step's fragments and,
+    // in the first FM + FN slots, the read of one fragment of k-step ks, so
+    // the LDS reads are spread over the matrix work instead of bunched in
+    // front of it (or sunk next to their first use, where the compiler puts
+    // them when left alone).  In the steady state the DMA of a later tile
+    // is spread over the first DMA_STEPS k-steps (one instruction after
+    // every MFMA_PER_DMA slots): a burst of DMA issues can stall the wave on
+    // a full memory queue while the matrix pipe runs dry, and with a
+    // 2-stage ring the loads must start early in the iteration to arrive
+    // before the next one.
+    constexpr int DMA_STEPS = (LPW + FM * FN - 1) / (FM * FN) > 1 ? KS : 1;
+    constexpr int DMA_WINDOW = DMA_STEPS * FM * FN;
+    constexpr int MFMA_PER_DMA = DMA_WINDOW / LPW > 0 ? DMA_WINDOW / LPW : 1;
+    static_assert(FM + FN <= FM * FN, "fragment reads fit in the slots");
     auto stage_body = [&](int st, bool dma, int64_t v_dma) {
-        load_frags(st, 0, fa[0], fb[0]);
+        const uint4 *as = lds + st * STAGE_SLOTS + (wm * TM + frag_row) * CPR;
+        const uint4 *bs = lds + st * STAGE_SLOTS + (BM + wn * TN + frag_row) * CPR;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int ks = 0; ks < KS; ++ks) {
+            const int cur = ks & 1, prev = cur ^ 1;
+            const int c = (ks * 2 + frag_half) ^ swz;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][i], fb[1][j], acc[i][j],
-                                                                    0, 0, 0);
-                const int n = i * FN + j;
-                if (dma && (n % MFMA_PER_DMA) == MFMA_PER_DMA - 1 && n / MFMA_PER_DMA < LPW) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    issue_dma_one(v_dma, n / MFMA_PER_DMA);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+            for (int n = 0; n < FM * FN; ++n) {
+                if (n < FM)
+                    fa[cur][n] = __builtin_bit_cast(bf16x8_t, as[n * 32 * CPR + c]);
+                else if (n < FM + FN)
+                    fb[cur][n - FM] = __builtin_bit_cast(bf16x8_t, bs[(n - FM) * 32 * CPR + c]);
+                const int i = n / FN, j = n % FN;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[prev][i], fb[prev][j],
+                                                                    acc[i][j], 0, 0, 0);
+                const int d = ks * FM * FN + n;
+                if (dma && (d % MFMA_PER_DMA) == MFMA_PER_DMA - 1 && d / MFMA_PER_DMA < LPW)
+                    issue_dma_one(v_dma, d / MFMA_PER_DMA);
+                __builtin_amdgcn_sched_barrier(0);
             }
-        load_frags(st, 1, fa[1], fb[1]);
-        mfma_step(fa[0], fb[0]);
+        }
     };
 
     // Barrier that the compiler may not move LDS accesses across.  It is
@@ -306,7 +335,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
             barrier();
             stage_body((int)(v % kStages), false, 0);
         }
-        mfma_step(fa[1], fb[1]);   // k-step 1 of the last stage
+        mfma_step(fa[1], fb[1]);   // last k-step of the last stage
         __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
         barrier();
     }
@@ -316,11 +345,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
     tile_epilogue<BM, BN, WM, WN>(g, tc, (float *)lds, m0, n0, acc);
 }
 
-template <int BM, int BN, int WM, int WN, int NS>
+template <int BM, int BN, int WM, int WN, int NS, int BK>
 hipError_t launch_one(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
-    const size_t lds_bytes = (size_t)NS * (BM + BN) * 4 * sizeof(uint4);
-    auto kern = gemm_mfma_bf16_kernel<BM, BN, WM, WN, NS>;
+    const size_t lds_bytes = (size_t)NS * (BM + BN) * (BK / 8) * sizeof(uint4);
+    auto kern = gemm_mfma_bf16_kernel<BM, BN, WM, WN, NS, BK>;
     hipLaunchKernelGGL(kern, dim3((unsigned)p.programs), dim3(64 * WM * WN), lds_bytes, stream,
                        g);
     return hipGetLastError();
@@ -330,22 +359,28 @@ hipError_t launch_one(const GemmArgs &g, const Plan &p, hipStream_t stream)
 
 // variant index -> instantiation (BM x BN tile, WM x WN wavefronts, ring depth)
 const TileConfig kMfmaBf16Tiles[] = {
-    {256, 256, MBK, 256, 0, "mfma_bf16_256x256x32_w2x2_s4"},
-    {128, 128, MBK, 256, 1, "mfma_bf16_128x128x32_w2x2_s4"},
-    {256, 128, MBK, 256, 2, "mfma_bf16_256x128x32_w2x2_s4"},
-    {256, 128, MBK, 256, 3, "mfma_bf16_256x128x32_w2x2_s3"},
-    {128, 256, MBK, 256, 4, "mfma_bf16_128x256x32_w2x2_s3"},
+    {256, 256, 32, 256, 0, "mfma_bf16_256x256x32_w2x2_s4"},
+    {128, 128, 32, 256, 1, "mfma_bf16_128x128x32_w2x2_s4"},
+    {256, 128, 32, 256, 2, "mfma_bf16_256x128x32_w2x2_s4"},
+    {256, 128, 32, 256, 3, "mfma_bf16_256x128x32_w2x2_s3"},
+    {128, 256, 32, 256, 4, "mfma_bf16_128x256x32_w2x2_s3"},
+    {256, 256, 64, 256, 5, "mfma_bf16_256x256x64_w2x2_s2"},
+    {128, 128, 64, 256, 6, "mfma_bf16_128x128x64_w2x2_s3"},
+    {256, 128, 64, 256, 7, "mfma_bf16_256x128x64_w2x2_s3"},
 };
-const int kNumMfmaBf16Tiles = 5;
+const int kNumMfmaBf16Tiles = 8;
 
 hipError_t launch_mfma_bf16(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
     switch (p.tile.variant) {
-    case 0: return launch_one<256, 256, 2, 2, 4>(g, p, stream);
-    case 1: return launch_one<128, 128, 2, 2, 4>(g, p, stream);
-    case 2: return launch_one<256, 128, 2, 2, 4>(g, p, stream);
-    case 3: return launch_one<256, 128, 2, 2, 3>(g, p, stream);
-    case 4: return launch_one<128, 256, 2, 2, 3>(g, p, stream);
+    case 0: return launch_one<256, 256, 2, 2, 4, 32>(g, p, stream);
+    case 1: return launch_one<128, 128, 2, 2, 4, 32>(g, p, stream);
+    case 2: return launch_one<256, 128, 2, 2, 4, 32>(g, p, stream);
+    case 3: return launch_one<256, 128, 2, 2, 3, 32>(g, p, stream);
+    case 4: return launch_one<128, 256, 2, 2, 3, 32>(g, p, stream);
+    case 5: return launch_one<256, 256, 2, 2, 2, 64>(g, p, stream);
+    case 6: return launch_one<128, 128, 2, 2, 3, 64>(g, p, stream);
+    case 7: return launch_one<256, 128, 2, 2, 3, 64>(g, p, stream);
     default: return hipErrorInvalidValue;
     }
 }
