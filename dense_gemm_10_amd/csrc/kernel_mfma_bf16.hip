@@ -264,11 +264,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
     // front of it (or sunk next to their first use, where the compiler puts
     // them when left alone).  In the steady state the DMA of a later tile
     // is spread over the first DMA_STEPS k-steps (one instruction after
-    // every MFMA_PER_DMA slots): a burst of DMA issues can stall the wave on
-    // a full memory queue while the matrix pipe runs dry, and with a
-    // 2-stage ring the loads must start early in the iteration to arrive
-    // before the next one.
-    constexpr int DMA_STEPS = (LPW + FM * FN - 1) / (FM * FN) > 1 ? KS : 1;
+    // every MFMA_PER_DMA slots): DMA instructions closer than about two
+    // MFMAs apart stall the in-order wave on the memory pipe while the
+    // matrix pipe runs dry, and with a 2-stage ring the loads must still
+    // start in the first half of the iteration to arrive before the next
+    // one (measured: first quarter 15 % slower, whole stage 23 % slower).
+#ifdef EXP_DMA_STEPS
+    constexpr int DMA_STEPS = EXP_DMA_STEPS <= KS ? EXP_DMA_STEPS : KS;
+#else
+    constexpr int DMA_STEPS = kStages == 2 ? KS / 2 : KS;
+#endif
+    static_assert(DMA_STEPS >= 1 && DMA_STEPS <= KS, "DMA window inside the stage");
     constexpr int DMA_WINDOW = DMA_STEPS * FM * FN;
     constexpr int MFMA_PER_DMA = DMA_WINDOW / LPW > 0 ? DMA_WINDOW / LPW : 1;
     static_assert(FM + FN <= FM * FN, "fragment reads fit in the slots");
@@ -358,13 +364,17 @@ hipError_t launch_one(const GemmArgs &g, const Plan &p, hipStream_t stream)
 } // namespace
 
 // variant index -> instantiation (BM x BN tile, WM x WN wavefronts, ring depth)
+// Entries 0 and 1 are the large and small tiles of the automatic choice:
+// 256 x 256 with whole-line (BK = 64) stages in a 2-stage ring, and
+// 128 x 128 with BK = 32 in a 4-stage ring (64 KB of LDS, two workgroups
+// per CU).  The others are selectable by name for sweeps.
 const TileConfig kMfmaBf16Tiles[] = {
-    {256, 256, 32, 256, 0, "mfma_bf16_256x256x32_w2x2_s4"},
+    {256, 256, 64, 256, 5, "mfma_bf16_256x256x64_w2x2_s2"},
     {128, 128, 32, 256, 1, "mfma_bf16_128x128x32_w2x2_s4"},
+    {256, 256, 32, 256, 0, "mfma_bf16_256x256x32_w2x2_s4"},
     {256, 128, 32, 256, 2, "mfma_bf16_256x128x32_w2x2_s4"},
     {256, 128, 32, 256, 3, "mfma_bf16_256x128x32_w2x2_s3"},
     {128, 256, 32, 256, 4, "mfma_bf16_128x256x32_w2x2_s3"},
-    {256, 256, 64, 256, 5, "mfma_bf16_256x256x64_w2x2_s2"},
     {128, 128, 64, 256, 6, "mfma_bf16_128x128x64_w2x2_s3"},
     {256, 128, 64, 256, 7, "mfma_bf16_256x128x64_w2x2_s3"},
 };
