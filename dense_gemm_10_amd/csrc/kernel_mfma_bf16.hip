@@ -269,11 +269,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
     // matrix pipe runs dry, and with a 2-stage ring the loads must still
     // start in the first half of the iteration to arrive before the next
     // one (measured: first quarter 15 % slower, whole stage 23 % slower).
-#ifdef EXP_DMA_STEPS
-    constexpr int DMA_STEPS = EXP_DMA_STEPS <= KS ? EXP_DMA_STEPS : KS;
-#else
     constexpr int DMA_STEPS = kStages == 2 ? KS / 2 : KS;
-#endif
     static_assert(DMA_STEPS >= 1 && DMA_STEPS <= KS, "DMA window inside the stage");
     constexpr int DMA_WINDOW = DMA_STEPS * FM * FN;
     constexpr int MFMA_PER_DMA = DMA_WINDOW / LPW > 0 ? DMA_WINDOW / LPW : 1;

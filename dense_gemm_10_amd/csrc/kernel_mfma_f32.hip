@@ -11,9 +11,12 @@
 //     A and column (l mod 32) of B at k = 2s + l/32 - is one float read by
 //     32 consecutive lanes from consecutive addresses;
 //   - global loads are 128-bit along each operand's contiguous dimension,
-//     masked on the row / column bound and the split's K range, and
-//     double-buffered through registers: tile t+1 is fetched while tile t
-//     is multiplied, one barrier per K tile (section 2.8).
+//     masked on the row / column bound and the split's K range only in
+//     edge tiles, and double-buffered through registers: tile t+1 is
+//     fetched while tile t is multiplied and written to the other LDS stage
+//     half-way through it, one barrier per K tile (section 2.8);
+//   - inside a K tile the fragment reads of each k-step are interleaved
+//     with the MFMAs of the previous one.
 // A 32x32x2 fp32 MFMA does 4096 flops in 64 cycles; per 16-deep K tile a
 // wave issues 8 k-steps of FM*FN MFMAs against 8*(FM+FN) one-float LDS
 // reads, so the kernel is bound by the matrix pipe, not by memory.
@@ -53,11 +56,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f32_kernel(GemmArgs g)
     constexpr int NT = 64 * WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int KSTEPS = FBK / 2;                        // MFMA k-steps per K tile
     constexpr int ALD = BM + FPAD, BLD = BN + FPAD;       // LDS row strides (floats)
     constexpr int A_STAGE = FBK * ALD, B_STAGE = FBK * BLD;
     // 128-bit loads per thread per K tile
     constexpr int A_VEC = BM * FBK / 4 / NT, B_VEC = BN * FBK / 4 / NT;
     static_assert(A_VEC * NT * 4 == BM * FBK && B_VEC * NT * 4 == BN * FBK, "load split");
+    static_assert(FM + FN <= FM * FN, "fragment reads fit in the slots");
 
     extern __shared__ float smem[];
     float *As = smem;                    // [2][FBK][ALD]
@@ -70,24 +75,50 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f32_kernel(GemmArgs g)
     split_range(g, tc.s, kb, ke);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const float *A = (const float *)g.A + tc.b * g.sa;
     const float *B = (const float *)g.B + tc.b * g.sb;
     const int64_t M = g.M, N = g.N, lda = g.lda, ldb = g.ldb;
+    // every row and column of the tile inside the matrices: no M / N masks
+    const bool interior = m0 + BM <= M && n0 + BN <= N;
 
     f32x16_t acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                acc[i][j][v] = 0.0f;
+            acc[i][j] = f32x16_t{};
 
     float4 ra[A_VEC], rb[B_VEC];
 
-    auto load_tiles = [&](int64_t k0) {
+    // Global -> registers, vector e (A vectors first, then B) of the K tile
+    // at k0, when the whole tile, K range included, lies inside the
+    // operands.  Issued one at a time between MFMAs (see tile_body).
+    constexpr int NVEC = A_VEC + B_VEC;
+    auto load_one = [&](int e, int64_t k0) {
+        if (e < A_VEC) {
+            const int idx = tid + e * NT;
+            if (!A_COL) {
+                const int r = idx / 4, kq = idx % 4;
+                ra[e] = *(const float4 *)(A + (m0 + r) * lda + k0 + kq * 4);
+            } else {
+                const int k = idx / (BM / 4), mq = idx % (BM / 4);
+                ra[e] = *(const float4 *)(A + (k0 + k) * lda + m0 + mq * 4);
+            }
+        } else {
+            const int idx = tid + (e - A_VEC) * NT;
+            if (!B_COL) {
+                const int k = idx / (BN / 4), nq = idx % (BN / 4);
+                rb[e - A_VEC] = *(const float4 *)(B + (k0 + k) * ldb + n0 + nq * 4);
+            } else {
+                const int n = idx / 4, kq = idx % 4;
+                rb[e - A_VEC] = *(const float4 *)(B + (n0 + n) * ldb + k0 + kq * 4);
+            }
+        }
+    };
+    // The whole K tile at k0 with the row / column and K masks (edge tiles).
+    auto load_tiles_masked = [&](int64_t k0) {
 #pragma unroll
         for (int e = 0; e < A_VEC; ++e) {
             const int idx = tid + e * NT;
@@ -116,11 +147,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f32_kernel(GemmArgs g)
         }
     };
 
-    auto store_tiles = [&](int st) {
+    // Registers -> LDS stage st, vector e (A vectors first, then B).
+    auto store_one = [&](int st, int e) {
         float *as = As + st * A_STAGE;
         float *bs = Bs + st * B_STAGE;
-#pragma unroll
-        for (int e = 0; e < A_VEC; ++e) {
+        if (e < A_VEC) {
             const int idx = tid + e * NT;
             if (!A_COL) {
                 const int r = idx / 4, kq = idx % 4;
@@ -132,59 +163,111 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f32_kernel(GemmArgs g)
                 const int k = idx / (BM / 4), mq = idx % (BM / 4);
                 *(float4 *)&as[k * ALD + mq * 4] = ra[e];
             }
-        }
-#pragma unroll
-        for (int e = 0; e < B_VEC; ++e) {
-            const int idx = tid + e * NT;
+        } else {
+            const int idx = tid + (e - A_VEC) * NT;
+            const float4 v = rb[e - A_VEC];
             if (!B_COL) {
                 const int k = idx / (BN / 4), nq = idx % (BN / 4);
-                *(float4 *)&bs[k * BLD + nq * 4] = rb[e];
+                *(float4 *)&bs[k * BLD + nq * 4] = v;
             } else {
                 const int n = idx / 4, kq = idx % 4;
-                bs[(kq * 4 + 0) * BLD + n] = rb[e].x;
-                bs[(kq * 4 + 1) * BLD + n] = rb[e].y;
-                bs[(kq * 4 + 2) * BLD + n] = rb[e].z;
-                bs[(kq * 4 + 3) * BLD + n] = rb[e].w;
+                bs[(kq * 4 + 0) * BLD + n] = v.x;
+                bs[(kq * 4 + 1) * BLD + n] = v.y;
+                bs[(kq * 4 + 2) * BLD + n] = v.z;
+                bs[(kq * 4 + 3) * BLD + n] = v.w;
+            }
+        }
+    };
+    auto store_tiles = [&](int st) {
+#pragma unroll
+        for (int e = 0; e < NVEC; ++e)
+            store_one(st, e);
+    };
+
+    // Fragments alternate between two register sets per k-step; fa[1] /
+    // fb[1] carry the last k-step of a tile across the barrier, where its
+    // MFMAs run while the next tile's first fragments are read.
+    const int frag = lane & 31, khalf = lane >> 5;
+    float fa[2][FM], fb[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+        fa[1][i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+        fb[1][j] = 0.0f;
+
+    // One K tile from stage st, as KSTEPS k-steps of FM * FN fenced slots:
+    // slot n issues the MFMA of block n on the previous k-step's fragments
+    // and, in the first FM + FN slots, the read of one fragment of this
+    // k-step (left alone, the compiler sinks the reads next to their use and
+    // the LDS latency stalls the matrix pipe).  When the next tile is
+    // loaded without masks (load_next), its global loads are issued one
+    // every SPREAD slots from the start of the tile, and its LDS stores one
+    // every SPREAD slots from k-step STORE_STEP: issued as one block, the
+    // loads of the four waves kept the matrix pipe idle for about a fifth
+    // of the loop.  Edge tiles load the next tile as one masked block
+    // before the body and store it at STORE_STEP (store_next).
+    constexpr int SLOTS = KSTEPS * FM * FN;
+    constexpr int SPREAD = 2;
+    constexpr int STORE_STEP = KSTEPS / 2;
+    static_assert(NVEC * SPREAD <= STORE_STEP * FM * FN, "loads issued before the stores");
+    static_assert(STORE_STEP * FM * FN + NVEC * SPREAD <= SLOTS, "stores inside the tile");
+    auto tile_body = [&](int st, bool load_next, int64_t k_next, bool store_next) {
+        const float *as = As + st * A_STAGE + wm * TM + frag;
+        const float *bs = Bs + st * B_STAGE + wn * TN + frag;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+            const int cur = s & 1, prev = cur ^ 1;
+            const int k = 2 * s + khalf;
+#pragma unroll
+            for (int n = 0; n < FM * FN; ++n) {
+                if (n < FM)
+                    fa[cur][n] = as[k * ALD + n * 32];
+                else if (n < FM + FN)
+                    fb[cur][n - FM] = bs[k * BLD + (n - FM) * 32];
+                const int i = n / FN, j = n % FN;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[prev][i], fb[prev][j],
+                                                                 acc[i][j], 0, 0, 0);
+                const int slot = s * FM * FN + n;
+                if (load_next && slot % SPREAD == SPREAD - 1 && slot / SPREAD < NVEC)
+                    load_one(slot / SPREAD, k_next);
+                const int ss = slot - STORE_STEP * FM * FN;
+                if ((load_next || store_next) && ss >= 0 && ss % SPREAD == SPREAD - 1 &&
+                    ss / SPREAD < NVEC)
+                    store_one(st ^ 1, ss / SPREAD);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
 
-    const int frag = lane & 31, khalf = lane >> 5;
-    auto compute = [&](int st) {
-        const float *as = As + st * A_STAGE + wm * TM + frag;
-        const float *bs = Bs + st * B_STAGE + wn * TN + frag;
-#pragma unroll
-        for (int s = 0; s < FBK / 2; ++s) {
-            const int k = 2 * s + khalf;
-            float a[FM], b[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                a[i] = as[k * ALD + i * 32];
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                b[j] = bs[k * BLD + j * 32];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-    };
-
     const int64_t nk = (ke > kb) ? (ke - kb + FBK - 1) / FBK : 0;
+    const int64_t nk_full = (ke - kb) / FBK;   // K tiles with all FBK k inside the split
     if (g.alpha != 0.0f && nk > 0) {
-        load_tiles(kb);
+        if (interior && nk_full >= 1) {
+#pragma unroll
+            for (int e = 0; e < NVEC; ++e)
+                load_one(e, kb);
+        } else {
+            load_tiles_masked(kb);
+        }
         store_tiles(0);
-        __syncthreads();
         for (int64_t kt = 0; kt < nk; ++kt) {
             const int st = (int)(kt & 1);
-            if (kt + 1 < nk)
-                load_tiles(kb + (kt + 1) * FBK);
-            compute(st);
-            if (kt + 1 < nk)
-                store_tiles(st ^ 1);
-            __syncthreads();
+            const bool has_next = kt + 1 < nk;
+            const bool fast_next = has_next && interior && kt + 1 < nk_full;
+            const int64_t k_next = kb + (kt + 1) * FBK;
+            lds_barrier();   // stage st complete; the stage written next no longer read
+            if (has_next && !fast_next)
+                load_tiles_masked(k_next);
+            tile_body(st, fast_next, k_next, has_next && !fast_next);
         }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)   // last k-step of the last tile
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[1][i], fb[1][j], acc[i][j],
+                                                                 0, 0, 0);
+        lds_barrier();
     }
 
     // the launch gives the kernel max(loop buffers, epilogue) bytes of LDS
