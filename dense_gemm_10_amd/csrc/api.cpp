@@ -335,14 +335,6 @@ void fill_args(const dg_gemm_desc *d, const Plan &p, const void *A, const void *
     g->act = d->act;
     g->write_partial = p.splits > 1;
     g->ab_bf16 = d->a_type == DG_BF16;
-    if (g->write_partial) {
-        // workspace rows are N floats; split and batch blocks are M*N floats
-        g->out_vec16 = ((uintptr_t)ws % 16 == 0) && d->N % 4 == 0;
-    } else {
-        const int64_t es = d->c_type == DG_BF16 ? 2 : 4;
-        g->out_vec16 = d->c_order == DG_ROW_MAJOR && ((uintptr_t)C % 16 == 0) &&
-                       (d->ldc * es) % 16 == 0 && (d->batch <= 1 || (d->stride_c * es) % 16 == 0);
-    }
     g->sched.num_pid_m = ceil_div(d->M, p.tile.bm);
     g->sched.num_pid_n = ceil_div(d->N, p.tile.bn);
     g->sched.batch = d->batch;

@@ -27,9 +27,6 @@ struct GemmArgs {
     int32_t act;                   // dg_act
     int32_t write_partial;         // 1: store raw fp32 partials to ws, no epilogue
     int32_t ab_bf16;               // input dtype of A and B: 1 = bf16, 0 = fp32
-    int32_t out_vec16;             // 1: the output (C, or ws when write_partial) is
-                                   // row-major and every row of every batch entry
-                                   // starts on a 16-byte boundary
     SchedArgs sched;
 };
 
@@ -61,14 +58,44 @@ __device__ __forceinline__ float load_as_f32(const void *base, int32_t is_bf16, 
 }
 
 // ---- activation ------------------------------------------------------------
+// GELU with the exact normal CDF, x * Phi(x), Phi(x) = erfc(-x / sqrt 2) / 2.
+// erfc on z = |x| / sqrt 2 follows Abramowitz and Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26: erfc(z) ~ t (a1 + t (a2 + t (a3 +
+// t (a4 + t a5)))) exp(-z^2) with t = 1 / (1 + p z), absolute error at most
+// 1.5e-7 for z >= 0.  Taking erfc directly (instead of 1 - erf) keeps the
+// negative side free of cancellation; one exp2, one reciprocal and no
+// branches, where the math library's erff is a long branchy sequence.
+__device__ __forceinline__ float gelu_erf(float x)
+{
+    const float z = fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+    float q = fmaf(t, 1.061405429f, -1.453152027f);
+    q = fmaf(t, q, 1.421413741f);
+    q = fmaf(t, q, -0.284496736f);
+    q = fmaf(t, q, 0.254829592f);
+    // exp(-z^2) = 2^(-x^2 log2(e) / 2)
+    const float e = __builtin_amdgcn_exp2f(-0.72134752044448170f * x * x);
+    const float h = 0.5f * t * q * e;          // erfc(z) / 2 = Phi(-|x|)
+    return x * (x >= 0.0f ? 1.0f - h : h);
+}
+
+// GELU with the tanh approximation of the normal CDF:
+// (1 + tanh(y)) / 2 with y = sqrt(2/pi) (x + 0.044715 x^3).  Uses the exact
+// identity (1 + tanh(y)) / 2 = 1 / (1 + exp(-2y)), which has no cancellation.
+__device__ __forceinline__ float gelu_tanh(float x)
+{
+    const float y = 0.79788456080286536f * fmaf(0.044715f * x, x * x, x);
+    // exp(-2y) = 2^(-2y log2(e))
+    const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * y);
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 __device__ __forceinline__ float activate(float x, int32_t act)
 {
     if (act == ACT_GELU_ERF)
-        return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));   // x * Phi(x)
-    if (act == ACT_GELU_TANH) {
-        const float s = 0.79788456080286536f;                          // sqrt(2/pi)
-        return 0.5f * x * (1.0f + tanhf(s * (x + 0.044715f * x * x * x)));
-    }
+        return gelu_erf(x);
+    if (act == ACT_GELU_TANH)
+        return gelu_tanh(x);
     return x;
 }
 

@@ -145,9 +145,12 @@ constexpr int epilogue_lds_bytes(int BN) { return (kEpilogueRows * epilogue_ld(B
 // the LDS chunk (fp32, row stride EP_LD).  Lane l's value v of a 32 x 32
 // block is row 8*(v/4) + 4*(l/32) + v%4, column l%32 of that block; wave
 // (wm, wn) owns blocks FM x FN at rows wm*TM + 32i, columns wn*TN + 32j.
-template <int BM, int BN, int WM, int WN>
+// Tile row r is stored shifted right by shift(r) < 8 floats (0 for the
+// generic path), with EP_LD leaving room for it.
+template <int BM, int BN, int WM, int WN, typename Shift>
 __device__ __forceinline__ void stage_chunk(float *chunk, int c,
-                                            const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
+                                            const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32],
+                                            Shift shift)
 {
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
@@ -160,83 +163,112 @@ __device__ __forceinline__ void stage_chunk(float *chunk, int c,
         const int row0 = wm * TM + i * 32 - c * EP_ROWS;   // block's first row in the chunk
         if (row0 >= 0 && row0 < EP_ROWS) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+            for (int v = 0; v < 16; ++v) {
+                const int row = row0 + 8 * (v / 4) + 4 * frag_half + (v % 4);
+                float *dst = chunk + row * EP_LD + shift(c * EP_ROWS + row) + wn * TN + (lane & 31);
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    chunk[(row0 + 8 * (v / 4) + 4 * frag_half + (v % 4)) * EP_LD + wn * TN + j * 32 +
-                          (lane & 31)] = acc[i][j][v];
+                for (int j = 0; j < FN; ++j)
+                    dst[j * 32] = acc[i][j][v];
+            }
         }
     }
 }
 
-// Epilogue of a tile that lies entirely inside the output, when every
-// output row starts on a 16-byte boundary (out_vec16): each thread turns
-// 16-byte runs of the staged chunk into one 16-byte store (8 bf16 or 4
-// fp32), with 32-bit offsets inside the tile and no per-element masks.
-// PARTIAL writes raw fp32 partials to the split-K workspace instead.
+// Epilogue of a tile of a row-major output (C, or the split-K workspace
+// when PARTIAL), at any alignment and with ragged edges.  Each output row
+// is cut into 16-byte aligned runs of VEC elements (8 bf16 or 4 fp32) at
+// its own alignment: a row whose first element sits delta elements past a
+// 16-byte boundary has a partial head run, BN / VEC - 1 full runs and a
+// partial tail.  The row is staged shifted by delta in LDS, so every run
+// reads one aligned 16-byte vector; full runs are written with one 16-byte
+// store (and read C with one 16-byte load when beta != 0), partial runs and
+// runs cut by the matrix edge element by element.
 template <int BM, int BN, int WM, int WN, bool PARTIAL, bool BF16_OUT>
-__device__ __forceinline__ void tile_epilogue_fast(const GemmArgs &g, const TileCoord &tc,
+__device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, const TileCoord &tc,
                                                    float *lds, int64_t m0, int64_t n0,
                                                    const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
 {
     constexpr int NT = 64 * WM * WN;
     constexpr int EP_ROWS = kEpilogueRows, EP_LD = epilogue_ld(BN);
-    constexpr int VEC = BF16_OUT ? 8 : 4;             // outputs per 16-byte store
-    constexpr int RUNS_PER_ROW = BN / VEC;
-    constexpr int RUNS = EP_ROWS * RUNS_PER_ROW;
-    static_assert(RUNS % NT == 0, "whole runs per thread");
+    constexpr int VEC = BF16_OUT ? 8 : 4;             // outputs per 16-byte run
+    constexpr int RPR = BN / VEC + 1;                 // runs per row (head + full + tail)
     constexpr int ES = BF16_OUT ? 2 : 4;              // output element size
+    static_assert(epilogue_ld(BN) >= BN + VEC - 1, "room for the row shift");
     const int tid = threadIdx.x;
     float *chunk = lds;
     float *bias_s = chunk + EP_ROWS * EP_LD;
     char *out;
-    int64_t ld_bytes;
+    int64_t ld;
     if (PARTIAL) {
-        out = (char *)(g.ws + ((int64_t)tc.s * g.sched.batch + tc.b) * g.M * g.N + m0 * g.N + n0);
-        ld_bytes = g.N * 4;
+        out = (char *)(g.ws + (((int64_t)tc.s * g.sched.batch + tc.b) * g.M + m0) * g.N + n0);
+        ld = g.N;
     } else {
         out = (char *)g.C + (tc.b * g.sc + m0 * g.ldc + n0) * ES;
-        ld_bytes = g.ldc * ES;
+        ld = g.ldc;
     }
+    const int64_t ld_bytes = ld * ES;
+    // misalignment (elements) of tile row r: (d0 + r * dl) mod VEC
+    const int d0 = (int)(((uintptr_t)out % 16) / ES);
+    const int dl = (int)(ld % VEC);
+    auto shift = [&](int r) { return (d0 + r * dl) & (VEC - 1); };
+    const int rows = (int)(g.M - m0 < BM ? g.M - m0 : BM);
+    const int cols = (int)(g.N - n0 < BN ? g.N - n0 : BN);
     const bool has_bias = !PARTIAL && g.bias;
     if (has_bias) {
         for (int t = tid; t < BN; t += NT)
-            bias_s[t] = load_as_f32(g.bias, g.bias_bf16, n0 + t);
+            bias_s[t] = t < cols ? load_as_f32(g.bias, g.bias_bf16, n0 + t) : 0.0f;
     }
 #pragma unroll
     for (int c = 0; c < BM / EP_ROWS; ++c) {
-        stage_chunk<BM, BN, WM, WN>(chunk, c, acc);
+        stage_chunk<BM, BN, WM, WN>(chunk, c, acc, shift);
         lds_barrier();
-#pragma unroll
-        for (int k = 0; k < RUNS / NT; ++k) {
-            const int r = tid + k * NT;
-            const int row = r / RUNS_PER_ROW;
-            const int col = (r % RUNS_PER_ROW) * VEC;
+        for (int r = tid; r < EP_ROWS * RPR; r += NT) {
+            const int row = r / RPR, j = r % RPR;
+            const int trow = c * EP_ROWS + row;                // tile row
+            const int c0 = j * VEC - shift(trow);              // tile column of element 0
+            const int lo = c0 < 0 ? -c0 : 0;
+            const int hi = cols - c0 < VEC ? cols - c0 : VEC;
+            if (trow >= rows || lo >= hi)
+                continue;
+            const bool full = lo == 0 && hi == VEC;
             float v[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; e += 4) {
-                const float4 q = *(const float4 *)&chunk[row * EP_LD + col + e];
+                const float4 q = *(const float4 *)&chunk[row * EP_LD + j * VEC + e];
                 v[e] = q.x; v[e + 1] = q.y; v[e + 2] = q.z; v[e + 3] = q.w;
             }
-            char *dst = out + (int64_t)(c * EP_ROWS + row) * ld_bytes + col * ES;
+            char *dst = out + (int64_t)trow * ld_bytes + (int64_t)c0 * ES;   // 16-byte aligned
             if (!PARTIAL) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
                     v[e] *= g.alpha;
                 if (g.beta != 0.0f) {
-                    const uint4 cin = *(const uint4 *)dst;
-                    const uint32_t w[4] = {cin.x, cin.y, cin.z, cin.w};
+                    if (full) {
+                        const uint4 cin = *(const uint4 *)dst;
+                        const uint32_t w[4] = {cin.x, cin.y, cin.z, cin.w};
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        const float x = BF16_OUT ? bf16_to_f32((uint16_t)(w[e / 2] >> (16 * (e % 2))))
-                                                 : __uint_as_float(w[e]);
-                        v[e] = fmaf(g.beta, x, v[e]);
+                        for (int e = 0; e < VEC; ++e) {
+                            const float x = BF16_OUT ? bf16_to_f32((uint16_t)(w[e / 2] >> (16 * (e % 2))))
+                                                     : __uint_as_float(w[e]);
+                            v[e] = fmaf(g.beta, x, v[e]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) {
+                            if (e >= lo && e < hi) {
+                                const float x = BF16_OUT ? bf16_to_f32(((const uint16_t *)dst)[e])
+                                                         : ((const float *)dst)[e];
+                                v[e] = fmaf(g.beta, x, v[e]);
+                            }
+                        }
                     }
                 }
                 if (has_bias) {
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        v[e] += bias_s[col + e];
+                    for (int e = 0; e < VEC; ++e) {
+                        const int col = c0 + e;
+                        v[e] += bias_s[col < 0 ? 0 : (col < BN ? col : BN - 1)];
+                    }
                 }
                 if (g.act != ACT_NONE) {
 #pragma unroll
@@ -245,13 +277,31 @@ __device__ __forceinline__ void tile_epilogue_fast(const GemmArgs &g, const Tile
                 }
             }
             if (BF16_OUT) {
-                uint32_t w[4];
+                uint16_t h[VEC];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = (uint32_t)f32_to_bf16(v[2 * e]) | ((uint32_t)f32_to_bf16(v[2 * e + 1]) << 16);
-                *(uint4 *)dst = make_uint4(w[0], w[1], w[2], w[3]);
+                for (int e = 0; e < VEC; ++e)
+                    h[e] = f32_to_bf16(v[e]);
+                if (full) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        w[e] = (uint32_t)h[2 * e] | ((uint32_t)h[2 * e + 1] << 16);
+                    *(uint4 *)dst = make_uint4(w[0], w[1], w[2], w[3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        if (e >= lo && e < hi)
+                            ((uint16_t *)dst)[e] = h[e];
+                }
             } else {
-                *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
+                if (full) {
+                    *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        if (e >= lo && e < hi)
+                            ((float *)dst)[e] = v[e];
+                }
             }
         }
         lds_barrier();
@@ -259,22 +309,23 @@ __device__ __forceinline__ void tile_epilogue_fast(const GemmArgs &g, const Tile
 }
 
 // Stage and store the whole tile.  `lds` must hold epilogue_lds_bytes(BN)
-// bytes and no wave may still be reading it for other purposes.  Tiles
-// inside the output with 16-byte aligned rows take tile_epilogue_fast; the
-// rest (ragged edges, column-major C, unaligned rows) go through the
-// masked, element-wise store_chunk.
+// bytes and no wave may still be reading it for other purposes.  Row-major
+// outputs (and split-K partials) take tile_epilogue_rows; a column-major C
+// goes through the masked, element-wise store_chunk.
 template <int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs &g, const TileCoord &tc, float *lds,
                                               int64_t m0, int64_t n0,
                                               const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
 {
-    if (g.out_vec16 && m0 + BM <= g.M && n0 + BN <= g.N) {
-        if (g.write_partial)
-            tile_epilogue_fast<BM, BN, WM, WN, true, false>(g, tc, lds, m0, n0, acc);
-        else if (g.c_bf16)
-            tile_epilogue_fast<BM, BN, WM, WN, false, true>(g, tc, lds, m0, n0, acc);
+    if (g.write_partial) {
+        tile_epilogue_rows<BM, BN, WM, WN, true, false>(g, tc, lds, m0, n0, acc);
+        return;
+    }
+    if (!g.c_col) {
+        if (g.c_bf16)
+            tile_epilogue_rows<BM, BN, WM, WN, false, true>(g, tc, lds, m0, n0, acc);
         else
-            tile_epilogue_fast<BM, BN, WM, WN, false, false>(g, tc, lds, m0, n0, acc);
+            tile_epilogue_rows<BM, BN, WM, WN, false, false>(g, tc, lds, m0, n0, acc);
         return;
     }
     constexpr int NT = 64 * WM * WN;
@@ -290,7 +341,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs &g, const TileCoord
     }
 #pragma unroll
     for (int c = 0; c < BM / EP_ROWS; ++c) {
-        stage_chunk<BM, BN, WM, WN>(chunk, c, acc);
+        stage_chunk<BM, BN, WM, WN>(chunk, c, acc, [](int) { return 0; });
         lds_barrier();
         if (g.write_partial)
             store_chunk<4, true, false, EP_ROWS, BN, EP_LD, NT>(g, tc, chunk, m0, n0, c * EP_ROWS,

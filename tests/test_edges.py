@@ -151,6 +151,29 @@ def test_bf16_output_ties_round_to_even(algo):
     assert got[0] == 0x3F80 and got[1] == 0x3F82
 
 
+@pytest.mark.parametrize("act", [W.ACT_GELU_ERF, W.ACT_GELU_TANH])
+@pytest.mark.parametrize("algo", [0, dg.DG_ALGO_GENERIC])
+def test_gelu_accuracy_on_a_dense_grid(act, algo):
+    # K = 1, B = 1: output (m, n) is act(x_m) of one exact fp32 value x_m,
+    # x on a dense grid of [-12, 12].  The erf form is held to the stated
+    # bound of its approximation of erfc (1.5e-7 absolute) scaled by |x|, the
+    # tanh form to the same bound, both with room for a few fp32 roundings.
+    M, N = 4096, 8
+    p = W.Problem(name="gelu", M=M, N=N, K=1, a_type=W.F32, b_type=W.F32, c_type=W.F32,
+                  alpha=1.0, beta=0.0, act=act)
+    xs = np.linspace(-12.0, 12.0, M).astype(np.float32)
+    x = W.make_inputs(p)
+    x.A[:] = W.lay_out(xs.reshape(1, M, 1), p.a_order, p.lda_, p.stride_a_,
+                       p.buffer_elems("a"), W.F32)
+    x.B[:] = W.lay_out(np.ones((1, 1, N), np.float32), p.b_order, p.ldb_, p.stride_b_,
+                       p.buffer_elems("b"), W.F32)
+    _, got = _run(p, x, algo=algo)
+    got = got[:M * p.ldc_].reshape(M, p.ldc_)[:, :N].astype(np.float64)
+    ref = np.array([oracle.act(float(v), act) for v in xs])
+    err = np.abs(got - ref[:, None]) / np.maximum(1.0, np.abs(xs.astype(np.float64)))[:, None]
+    assert err.max() <= 4e-7, (err.max(), xs[int(np.argmax(err.max(axis=1)))])
+
+
 @pytest.mark.parametrize("name", ["c3", "c5"])
 def test_run_to_run_bitwise_determinism(name):
     from workloads.device import DeviceProblem
