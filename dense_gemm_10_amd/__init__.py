@@ -39,6 +39,7 @@ DG_F32, DG_BF16 = 0, 1
 DG_ROW_MAJOR, DG_COL_MAJOR = 0, 1
 DG_ACT_NONE, DG_ACT_GELU_ERF, DG_ACT_GELU_TANH = 0, 1, 2
 DG_ALGO_AUTO, DG_ALGO_GENERIC, DG_ALGO_VALU_F32, DG_ALGO_MFMA_BF16, DG_ALGO_MFMA_F32 = range(5)
+DG_SCHED_AUTO, DG_SCHED_DATA_PARALLEL, DG_SCHED_STREAM_K = range(3)
 
 _DTYPE = {"f32": DG_F32, "bf16": DG_BF16}
 _ORDER = {"row": DG_ROW_MAJOR, "col": DG_COL_MAJOR}
@@ -59,7 +60,7 @@ class DgGemmDesc(ctypes.Structure):
         ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
         ("bias", ctypes.c_void_p),
         ("act", ctypes.c_int32), ("split_k", ctypes.c_int32), ("group_m", ctypes.c_int32),
-        ("algo", ctypes.c_int32), ("xcd_remap", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("algo", ctypes.c_int32), ("xcd_remap", ctypes.c_int32), ("schedule", ctypes.c_int32),
     ]
 
 
@@ -115,7 +116,7 @@ def make_desc(M, N, K, batch=1, a_type="f32", b_type=None, c_type=None,
               a_order="row", b_order="row", c_order="row", lda=None, ldb=None, ldc=None,
               stride_a=None, stride_b=None, stride_c=None, alpha=1.0, beta=0.0,
               bias=None, bias_type="f32", act="none", split_k=0, group_m=0, algo=0,
-              xcd_remap=0):
+              xcd_remap=0, schedule=0):
     """Fill a DgGemmDesc.  Leading dimensions default to the packed value
     and batch strides to the packed matrix size; ``bias`` is a device
     address (int) or None."""
@@ -146,6 +147,7 @@ def make_desc(M, N, K, batch=1, a_type="f32", b_type=None, c_type=None,
     d.bias = bias
     d.act = _enum(_ACT, act)
     d.split_k, d.group_m, d.algo, d.xcd_remap = split_k, group_m, algo, xcd_remap
+    d.schedule = schedule
     return d
 
 

@@ -28,6 +28,8 @@ struct GemmArgs {
     int32_t write_partial;         // 1: store raw fp32 partials to ws, no epilogue
     int32_t ab_bf16;               // input dtype of A and B: 1 = bf16, 0 = fp32
     SchedArgs sched;
+    StreamK sk;                    // sk.tail_tiles == 0: data-parallel launch
+    float *sk_parts;               // stream-K partials, [tail tile][slice][BM * BN] fp32
 };
 
 enum { ACT_NONE = 0, ACT_GELU_ERF = 1, ACT_GELU_TANH = 2 };

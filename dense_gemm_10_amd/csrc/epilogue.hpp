@@ -183,9 +183,12 @@ __device__ __forceinline__ void stage_chunk(float *chunk, int c,
 // reads one aligned 16-byte vector; full runs are written with one 16-byte
 // store (and read C with one 16-byte load when beta != 0), partial runs and
 // runs cut by the matrix edge element by element.
+// `out` points at the tile's first element, `ld` is the output's row
+// stride (elements), rows x cols the part of the tile inside the output and
+// n0 the tile's first column (for the bias).
 template <int BM, int BN, int WM, int WN, bool PARTIAL, bool BF16_OUT>
-__device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, const TileCoord &tc,
-                                                   float *lds, int64_t m0, int64_t n0,
+__device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out, int64_t ld,
+                                                   int rows, int cols, int64_t n0, float *lds,
                                                    const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
 {
     constexpr int NT = 64 * WM * WN;
@@ -197,22 +200,11 @@ __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, const Tile
     const int tid = threadIdx.x;
     float *chunk = lds;
     float *bias_s = chunk + EP_ROWS * EP_LD;
-    char *out;
-    int64_t ld;
-    if (PARTIAL) {
-        out = (char *)(g.ws + (((int64_t)tc.s * g.sched.batch + tc.b) * g.M + m0) * g.N + n0);
-        ld = g.N;
-    } else {
-        out = (char *)g.C + (tc.b * g.sc + m0 * g.ldc + n0) * ES;
-        ld = g.ldc;
-    }
     const int64_t ld_bytes = ld * ES;
     // misalignment (elements) of tile row r: (d0 + r * dl) mod VEC
     const int d0 = (int)(((uintptr_t)out % 16) / ES);
     const int dl = (int)(ld % VEC);
     auto shift = [&](int r) { return (d0 + r * dl) & (VEC - 1); };
-    const int rows = (int)(g.M - m0 < BM ? g.M - m0 : BM);
-    const int cols = (int)(g.N - n0 < BN ? g.N - n0 : BN);
     const bool has_bias = !PARTIAL && g.bias;
     if (has_bias) {
         for (int t = tid; t < BN; t += NT)
@@ -317,15 +309,24 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs &g, const TileCoord
                                               int64_t m0, int64_t n0,
                                               const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
 {
+    const int rows = (int)(g.M - m0 < BM ? g.M - m0 : BM);
+    const int cols = (int)(g.N - n0 < BN ? g.N - n0 : BN);
     if (g.write_partial) {
-        tile_epilogue_rows<BM, BN, WM, WN, true, false>(g, tc, lds, m0, n0, acc);
+        float *out = g.ws + (((int64_t)tc.s * g.sched.batch + tc.b) * g.M + m0) * g.N + n0;
+        tile_epilogue_rows<BM, BN, WM, WN, true, false>(g, (char *)out, g.N, rows, cols, n0, lds,
+                                                        acc);
         return;
     }
     if (!g.c_col) {
-        if (g.c_bf16)
-            tile_epilogue_rows<BM, BN, WM, WN, false, true>(g, tc, lds, m0, n0, acc);
-        else
-            tile_epilogue_rows<BM, BN, WM, WN, false, false>(g, tc, lds, m0, n0, acc);
+        if (g.c_bf16) {
+            char *out = (char *)g.C + (tc.b * g.sc + m0 * g.ldc + n0) * 2;
+            tile_epilogue_rows<BM, BN, WM, WN, false, true>(g, out, g.ldc, rows, cols, n0, lds,
+                                                            acc);
+        } else {
+            char *out = (char *)g.C + (tc.b * g.sc + m0 * g.ldc + n0) * 4;
+            tile_epilogue_rows<BM, BN, WM, WN, false, false>(g, out, g.ldc, rows, cols, n0, lds,
+                                                             acc);
+        }
         return;
     }
     constexpr int NT = 64 * WM * WN;

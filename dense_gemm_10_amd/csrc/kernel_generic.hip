@@ -130,6 +130,38 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int32_t 
     }
 }
 
+// Stream-K fix-up: each tail tile left tail_splits fp32 partials in the
+// workspace, one per K slice; add them in slice order (a fixed order, so
+// the result is reproducible) and apply the epilogue once.
+__global__ __launch_bounds__(256) void streamk_fixup_kernel(GemmArgs g, int32_t bm, int32_t bn)
+{
+    const int64_t area = (int64_t)bm * bn;                 // a multiple of 1024
+    const int64_t per_tile = area / 1024;                  // blocks per tile, 4 outputs per thread
+    const int64_t r = blockIdx.x / per_tile;
+    const int64_t e0 = (blockIdx.x % per_tile) * 1024 + threadIdx.x * 4;
+    const TileCoord tc = decode_tile(g.sk.dp_tiles + r, g.sched);
+    const int64_t m0 = (int64_t)tc.pid_m * bm, n0 = (int64_t)tc.pid_n * bn;
+    const int64_t row = e0 / bn, col = e0 % bn;            // 4 consecutive columns of one row
+    const int64_t m = m0 + row;
+    if (m >= g.M)
+        return;
+    const float *p = g.sk_parts + r * g.sk.tail_splits * area + e0;
+    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t s = 0; s < g.sk.tail_splits; ++s) {
+        const float4 v = *(const float4 *)(p + s * area);
+        sum[0] += v.x;
+        sum[1] += v.y;
+        sum[2] += v.z;
+        sum[3] += v.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + col + j;
+        if (n < g.N)
+            store_c(g, 0, m, n, epilogue_value(g, 0, m, n, sum[j]));
+    }
+}
+
 } // namespace
 
 const TileConfig kGenericTiles[] = {
@@ -145,6 +177,13 @@ hipError_t launch_generic(const GemmArgs &g, const Plan &p, hipStream_t stream)
         hipLaunchKernelGGL((gemm_generic_kernel<true, true>), grid, block, 0, stream, g);
     else
         hipLaunchKernelGGL((gemm_generic_kernel<false, false>), grid, block, 0, stream, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_streamk_fixup(const GemmArgs &g, const Plan &p, hipStream_t stream)
+{
+    dim3 grid((unsigned)p.fixup_blocks), block(256);
+    hipLaunchKernelGGL(streamk_fixup_kernel, grid, block, 0, stream, g, p.tile.bm, p.tile.bn);
     return hipGetLastError();
 }
 

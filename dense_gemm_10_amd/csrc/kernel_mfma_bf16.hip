@@ -117,8 +117,12 @@ __device__ __forceinline__ int swizzle_key(int r)
     return (r / (16 / CPR)) % CPR;
 }
 
+// One output tile (or, for stream-K, one K range of it): K loop over
+// [kb, ke) and the epilogue, or the raw fp32 accumulators written to `part`
+// (a BM x BN row-major slot) when `part` is not null.
 template <int BM, int BN, int WM, int WN, int kStages, int MBK>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g)
+__device__ __forceinline__ void mfma_bf16_tile(const GemmArgs &g, TileCoord tc, int64_t kb,
+                                               int64_t ke, float *part, uint4 *lds)
 {
     constexpr int NT = 64 * WM * WN;
     constexpr int NW = WM * WN;
@@ -137,18 +141,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
     static_assert(BM % RPI == 0 && BN % RPI == 0 && GROUPS % NW == 0, "DMA split");
 
-    extern __shared__ uint4 lds[];
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)lds;
 
-    TileCoord tc = decode_program(blockIdx.x, g.sched);
     tc.b = uniform_i64(tc.b);
     tc.s = __builtin_amdgcn_readfirstlane(tc.s);
     tc.pid_m = __builtin_amdgcn_readfirstlane(tc.pid_m);
     tc.pid_n = __builtin_amdgcn_readfirstlane(tc.pid_n);
     const int64_t m0 = (int64_t)tc.pid_m * BM;
     const int64_t n0 = (int64_t)tc.pid_n * BN;
-    int64_t kb, ke;
-    split_range(g, tc.s, kb, ke);
+    kb = uniform_i64(kb);
+    ke = uniform_i64(ke);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -344,7 +346,45 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
 
     static_assert(epilogue_lds_bytes(BN) <= kStages * STAGE_SLOTS * 16,
                   "epilogue chunk and bias fit in LDS");
-    tile_epilogue<BM, BN, WM, WN>(g, tc, (float *)lds, m0, n0, acc);
+    if (part)
+        tile_epilogue_rows<BM, BN, WM, WN, true, false>(g, (char *)part, BN, BM, BN, n0,
+                                                        (float *)lds, acc);
+    else
+        tile_epilogue<BM, BN, WM, WN>(g, tc, (float *)lds, m0, n0, acc);
+}
+
+// Data-parallel launches give each program one tile (or split-K slice).
+// Stream-K launches give programs [0, dp_tiles) one whole tile each and the
+// others one K slice of a tail tile, written as a raw fp32 partial that the
+// fix-up kernel adds up.
+template <int BM, int BN, int WM, int WN, int kStages, int MBK>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g)
+{
+    extern __shared__ uint4 lds[];
+    const StreamK &sk = g.sk;
+    const int64_t pid = blockIdx.x;
+    TileCoord tc;
+    int64_t kb, ke;
+    float *part = nullptr;
+    if (sk.tail_tiles == 0) {
+        tc = decode_program(pid, g.sched);
+        split_range(g, tc.s, kb, ke);
+    } else if (pid < sk.dp_tiles) {
+        tc = decode_tile(g.sched.xcd_remap ? xcd_remap(pid, sk.dp_tiles) : pid, g.sched);
+        kb = 0;
+        ke = g.K;
+    } else {
+        // dp_tiles is a multiple of 8, so the remap keeps each program on
+        // its XCD; an XCD's programs then share slices and tile rows.
+        const int64_t n = sk.tail_tiles * sk.tail_splits;
+        const int64_t i = g.sched.xcd_remap ? xcd_remap(pid - sk.dp_tiles, n) : pid - sk.dp_tiles;
+        const int64_t slice = i / sk.tail_tiles, r = i % sk.tail_tiles;
+        tc = decode_tile(sk.dp_tiles + r, g.sched);
+        kb = slice * sk.k_per_split;
+        ke = kb + sk.k_per_split < g.K ? kb + sk.k_per_split : g.K;
+        part = g.sk_parts + (r * sk.tail_splits + slice) * (int64_t)(BM * BN);
+    }
+    mfma_bf16_tile<BM, BN, WM, WN, kStages, MBK>(g, tc, kb, ke, part, lds);
 }
 
 template <int BM, int BN, int WM, int WN, int NS, int BK>
@@ -365,14 +405,14 @@ hipError_t launch_one(const GemmArgs &g, const Plan &p, hipStream_t stream)
 // 128 x 128 with BK = 32 in a 4-stage ring (64 KB of LDS, two workgroups
 // per CU).  The others are selectable by name for sweeps.
 const TileConfig kMfmaBf16Tiles[] = {
-    {256, 256, 64, 256, 5, "mfma_bf16_256x256x64_w2x2_s2"},
-    {128, 128, 32, 256, 1, "mfma_bf16_128x128x32_w2x2_s4"},
-    {256, 256, 32, 256, 0, "mfma_bf16_256x256x32_w2x2_s4"},
-    {256, 128, 32, 256, 2, "mfma_bf16_256x128x32_w2x2_s4"},
-    {256, 128, 32, 256, 3, "mfma_bf16_256x128x32_w2x2_s3"},
-    {128, 256, 32, 256, 4, "mfma_bf16_128x256x32_w2x2_s3"},
-    {128, 128, 64, 256, 6, "mfma_bf16_128x128x64_w2x2_s3"},
-    {256, 128, 64, 256, 7, "mfma_bf16_256x128x64_w2x2_s3"},
+    {256, 256, 64, 256, 5, "mfma_bf16_256x256x64_w2x2_s2", 1},
+    {128, 128, 32, 256, 1, "mfma_bf16_128x128x32_w2x2_s4", 2},
+    {256, 256, 32, 256, 0, "mfma_bf16_256x256x32_w2x2_s4", 1},
+    {256, 128, 32, 256, 2, "mfma_bf16_256x128x32_w2x2_s4", 1},
+    {256, 128, 32, 256, 3, "mfma_bf16_256x128x32_w2x2_s3", 1},
+    {128, 256, 32, 256, 4, "mfma_bf16_128x256x32_w2x2_s3", 1},
+    {128, 128, 64, 256, 6, "mfma_bf16_128x128x64_w2x2_s3", 1},
+    {256, 128, 64, 256, 7, "mfma_bf16_256x128x64_w2x2_s3", 1},
 };
 const int kNumMfmaBf16Tiles = 8;
 

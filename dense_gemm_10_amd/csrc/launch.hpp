@@ -20,6 +20,7 @@ struct TileConfig {
     int32_t threads;
     int32_t variant;     // index into the family's instantiation table
     const char *name;
+    int32_t per_cu;      // workgroups one CU holds at once (LDS and registers)
 };
 
 struct Plan {
@@ -30,6 +31,8 @@ struct Plan {
     int64_t programs;        // grid size of the main kernel
     size_t workspace_bytes;  // 0 unless splits > 1
     int64_t reduce_blocks;   // grid of the split-K reduction (0 if none)
+    StreamK sk;              // sk.tail_tiles > 0: stream-K launch
+    int64_t fixup_blocks;    // grid of the stream-K fix-up (0 if none)
 };
 
 // Launchers: enqueue the kernel on `stream`; return hipSuccess or the
@@ -39,6 +42,7 @@ hipError_t launch_valu_f32(const GemmArgs &g, const Plan &p, hipStream_t stream)
 hipError_t launch_mfma_bf16(const GemmArgs &g, const Plan &p, hipStream_t stream);
 hipError_t launch_mfma_f32(const GemmArgs &g, const Plan &p, hipStream_t stream);
 hipError_t launch_splitk_reduce(const GemmArgs &g, const Plan &p, hipStream_t stream);
+hipError_t launch_streamk_fixup(const GemmArgs &g, const Plan &p, hipStream_t stream);
 
 // Tile configurations of each family (defined next to the kernels).
 extern const TileConfig kGenericTiles[];

@@ -62,26 +62,49 @@ DG_HD inline int64_t xcd_remap(int64_t pid, int64_t P)
     return x * q + (x < r ? x : r) + pid / kNumXcd;
 }
 
-DG_HD inline TileCoord decode_program(int64_t pid, const SchedArgs &a)
+// Group-M swizzle of tile index t (0 <= t < num_pid_m * num_pid_n) into
+// (pid_m, pid_n); b and s are left 0.
+DG_HD inline TileCoord decode_tile(int64_t t, const SchedArgs &a)
 {
-    const int64_t T = a.num_pid_m * a.num_pid_n;
-    const int64_t P = a.batch * (int64_t)a.splits * T;
-    const int64_t L = a.xcd_remap ? xcd_remap(pid, P) : pid;
-    const int64_t t = L % T;
-    const int64_t bs = L / T;
-    TileCoord c;
-    c.s = (int32_t)(bs % a.splits);
-    c.b = bs / a.splits;
-    // group-M swizzle of the tile index t
     const int64_t in_group = (int64_t)a.group_m * a.num_pid_n;
     const int64_t group_id = t / in_group;
     const int64_t first_m = group_id * a.group_m;
     int64_t rows = a.num_pid_m - first_m;
     if (rows > a.group_m)
         rows = a.group_m;
+    TileCoord c;
+    c.b = 0;
+    c.s = 0;
     c.pid_m = (int32_t)(first_m + t % rows);
     c.pid_n = (int32_t)((t % in_group) / rows);
     return c;
 }
+
+DG_HD inline TileCoord decode_program(int64_t pid, const SchedArgs &a)
+{
+    const int64_t T = a.num_pid_m * a.num_pid_n;
+    const int64_t P = a.batch * (int64_t)a.splits * T;
+    const int64_t L = a.xcd_remap ? xcd_remap(pid, P) : pid;
+    const int64_t bs = L / T;
+    TileCoord c = decode_tile(L % T, a);
+    c.s = (int32_t)(bs % a.splits);
+    c.b = bs / a.splits;
+    return c;
+}
+
+// Stream-K tail (one matrix, no split-K): the tiles of the full waves,
+// [0, dp_tiles), are computed whole by programs [0, dp_tiles); each of the
+// tail_tiles remaining tiles has its K range cut into tail_splits slices of
+// k_per_split (a multiple of the kernel's BK), one program per slice, which
+// writes a raw fp32 partial.  Tail program i (0 <= i < tail_tiles *
+// tail_splits, after the XCD remap) takes slice i / tail_tiles of tail tile
+// i % tail_tiles: programs with the same slice read the same K range of
+// their A and B panels.
+struct StreamK {
+    int64_t dp_tiles;
+    int64_t tail_tiles;       // 0: plain data-parallel launch
+    int64_t tail_splits;
+    int64_t k_per_split;
+};
 
 } // namespace dg

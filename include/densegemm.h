@@ -84,6 +84,26 @@ typedef enum {
     DG_ALGO_MFMA_F32 = 4   /* fp32 matrix-core kernel */
 } dg_algo;
 
+/* Work distribution over the compute units (benchmarking and ablation; 0
+ * lets the library choose).  DATA_PARALLEL gives every output tile (and
+ * split-K slice) to one workgroup.  STREAM_K splits work along K to keep
+ * the last wave busy ("La GEMM, de zero a cuBLAS", section 2.10, on
+ * Stream-K and wave quantisation): the tiles of the full waves stay
+ * data-parallel, and the K range of each remaining (tail) tile is cut into
+ * slices, one workgroup each, enough to fill one more wave; a second, small
+ * kernel adds each tail tile's fp32 partials in slice order (fixed order, no
+ * atomics) and applies the epilogue.  STREAM_K applies to the bf16
+ * matrix-core kernel with batch == 1 and split_k <= 1 and needs workspace
+ * (see dg_gemm_workspace_size); otherwise DG_ERROR_NOT_SUPPORTED.  The
+ * automatic choice uses it only for that kernel, when the last wave of
+ * tiles would be less than 85 % full, K >= 2048 and the caller passes
+ * enough workspace. */
+typedef enum {
+    DG_SCHED_AUTO = 0,
+    DG_SCHED_DATA_PARALLEL = 1,
+    DG_SCHED_STREAM_K = 2
+} dg_schedule;
+
 /*
  * Problem descriptor.  All integer fields are in ELEMENTS, not bytes.
  *
@@ -114,6 +134,7 @@ typedef enum {
  *   xcd_remap       1 (default when 0) spreads consecutive tile groups over
  *                   the chip's 8 XCDs so each XCD's L2 sees a contiguous
  *                   part of the swizzled order; -1 disables it.
+ *   schedule        dg_schedule; 0 = automatic choice.
  */
 typedef struct dg_gemm_desc {
     uint32_t struct_size;
@@ -130,7 +151,7 @@ typedef struct dg_gemm_desc {
     int32_t group_m;
     int32_t algo;      /* dg_algo */
     int32_t xcd_remap;
-    int32_t reserved;
+    int32_t schedule;  /* dg_schedule */
 } dg_gemm_desc;
 
 /* Library version, DG_VERSION of the build. */
@@ -140,8 +161,8 @@ int dg_version(void);
 const char *dg_status_string(dg_status s);
 
 /* Device bytes of workspace that dg_gemm would use for `d` (0 when the
- * chosen plan needs none).  With split_k == 0 this is the size that lets
- * the library pick split-K where it pays.  Returns INVALID_VALUE /
+ * chosen plan needs none).  With split_k == 0 and schedule == 0 this is the
+ * size that lets the library pick split-K or Stream-K where they pay.  Returns INVALID_VALUE /
  * NOT_SUPPORTED for descriptors dg_gemm would reject. */
 dg_status dg_gemm_workspace_size(const dg_gemm_desc *d, size_t *bytes);
 
@@ -150,10 +171,10 @@ dg_status dg_gemm_workspace_size(const dg_gemm_desc *d, size_t *bytes);
  *              and written); they must be aligned to their element size.
  *              C must not overlap A, B or bias.  A and B may be NULL when
  *              alpha == 0 or K == 0.
- *   workspace  device scratch of workspace_bytes (may be NULL / 0).  The
- *              library writes it; its content before and after is
- *              unspecified.  It must not be used by other work until this
- *              call's work has completed on `stream`.
+ *   workspace  device scratch of workspace_bytes (may be NULL / 0),
+ *              16-byte aligned.  The library writes it; its content before
+ *              and after is unspecified.  It must not be used by other work
+ *              until this call's work has completed on `stream`.
  *   stream     a hipStream_t (passed as void*), NULL for the null stream.
  * Returns DG_SUCCESS once the work is enqueued. */
 dg_status dg_gemm(const dg_gemm_desc *d, const void *A, const void *B, void *C,

@@ -7,6 +7,7 @@ import re
 import subprocess
 import tempfile
 
+import numpy as np
 import pytest
 
 import dense_gemm_10_amd as dg
@@ -153,6 +154,7 @@ def test_forced_split_needs_workspace():
     d = _desc(K=4096, split_k=4)
     need = dg.dg_gemm_workspace_size(d)
     assert need == 4 * 64 * 48 * 4
+    assert "reduce_blocks=12 " in dg.dg_gemm_describe(d, need)     # 64 * 48 outputs / 256
     assert _gemm_status(d) == dg.DG_ERROR_INSUFFICIENT_WORKSPACE
     assert _gemm_status(d, ws=PW, ws_bytes=need - 4) == dg.DG_ERROR_INSUFFICIENT_WORKSPACE
     # workspace overlapping C
@@ -212,3 +214,61 @@ def test_batch_strides_ignored_for_a_single_matrix():
 def test_k_zero_and_alpha_zero_never_split():
     assert "splits=1 " in dg.dg_gemm_describe(_desc(K=0, split_k=8, lda=1), 1 << 30)
     assert "splits=1 " in dg.dg_gemm_describe(_desc(K=8192, alpha=0.0, split_k=8), 1 << 30)
+
+
+def _sk_fields(text):
+    kv = dict(t.split("=", 1) for t in text.split() if "=" in t)
+    return {k: int(kv[k]) for k in ("dp_tiles", "tail_tiles", "tail_splits", "tail_k_per_split")}
+
+
+def test_stream_k_plan_for_a_badly_quantised_grid():
+    # the GELU workload's grid with a long K (the automatic choice wants K >= 2048)
+    d = _desc_for(W.WORKLOADS["c4"].replace(K=4096))
+    ws = dg.dg_gemm_workspace_size(d)
+    text = dg.dg_gemm_describe(d, ws)
+    assert "schedule=stream_k" in text and "bm=128 bn=128" in text
+    sk = _sk_fields(text)
+    # 4095 x 4097 in 128 x 128 tiles = 1056; one wave is 2 x 256 = 512
+    assert sk["dp_tiles"] == 1024 and sk["tail_tiles"] == 32
+    assert "fixup_blocks=%d " % (32 * 16) in text
+    assert sk["tail_splits"] == 16 and sk["tail_k_per_split"] == 256   # K = 4096
+    assert "programs=%d " % (1024 + 32 * 16) in text
+    assert ws == 32 * 16 * 128 * 128 * 4
+    # without workspace, or with K < 2048, the automatic choice stays data-parallel
+    assert "schedule=data_parallel" in dg.dg_gemm_describe(d, 0)
+    assert "schedule=data_parallel" in dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c4"]), 1 << 34)
+    # a whole number of waves stays data-parallel
+    assert "schedule=data_parallel" in dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c3"]), 1 << 30)
+
+
+def test_stream_k_slices_cover_k_once():
+    for M, N, K in [(4095, 4097, 1000), (640, 640, 1024), (2944, 2944, 4096), (4352, 4352, 200)]:
+        d = _desc(M=M, N=N, K=K, a_type="bf16", b_order="col", schedule=dg.DG_SCHED_STREAM_K)
+        sk = _sk_fields(dg.dg_gemm_describe(d, 1 << 34))
+        S, kps = sk["tail_splits"], sk["tail_k_per_split"]
+        assert S >= 2 and kps % 32 == 0
+        assert (S - 1) * kps < K <= S * kps          # every slice non-empty, all of K covered
+
+
+def test_stream_k_requirements():
+    sk = dict(schedule=dg.DG_SCHED_STREAM_K)
+    # only the bf16 matrix-core kernel, one matrix, no split-K
+    for bad in [_desc(**sk), _desc(a_type="bf16", b_order="col", batch=2, **sk),
+                _desc(a_type="bf16", b_order="col", K=4096, split_k=4, **sk)]:
+        with pytest.raises(dg.DgError) as e:
+            dg.dg_gemm_describe(bad, 1 << 30)
+        assert e.value.status == dg.DG_ERROR_NOT_SUPPORTED
+    d = _desc(M=3000, N=3000, K=256, a_type="bf16", b_order="col", **sk)
+    need = dg.dg_gemm_workspace_size(d)
+    assert need > 0
+    big = dict(A=1 << 40, B=2 << 40, C=3 << 40)     # far apart: no operand overlap
+    assert _gemm_status(d, **big) == dg.DG_ERROR_INSUFFICIENT_WORKSPACE
+    assert _gemm_status(d, ws=4 << 40, ws_bytes=need - 16, **big) == \
+        dg.DG_ERROR_INSUFFICIENT_WORKSPACE
+    assert _gemm_status(d, ws=(4 << 40) + 8, ws_bytes=need, **big) == \
+        dg.DG_ERROR_INVALID_VALUE                    # the workspace must be 16-byte aligned
+    bad = _desc(schedule=3)
+    assert _gemm_status(bad) == dg.DG_ERROR_INVALID_VALUE
+    # data-parallel on request
+    d4 = _desc_for(W.WORKLOADS["c4"], schedule=dg.DG_SCHED_DATA_PARALLEL)
+    assert "schedule=data_parallel" in dg.dg_gemm_describe(d4, 1 << 34)
