@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the dense GEMM library on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5]
+    python bench.py [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5|flat16|...]
 
 A step is one call of the library (dg_gemm through the C ABI) on one
 workload whose operands are already resident in HBM: scheduler, loader,
@@ -42,19 +42,20 @@ def _dtype_name(p):
 
 
 def _roofline_peak(p, kernel):
-    """(bound, peak FLOP/s) of the workload's dominant kernel."""
+    """(bound, peak) of the workload's dominant kernel: its compute peak
+    (matrix cores for the MFMA kernels, the unpacked vector-FMA rate for
+    the others), or HBM when the algorithmic bytes take longer at 8 TB/s
+    than the flops at that peak."""
     from dense_gemm_10_amd import accounting as acc
-    if kernel == "valu_f32":
-        return "alu", acc.PEAK_F32_VALU_UNPACKED
     if kernel.startswith("mfma_bf16"):
-        t_c = acc.problem_flops(p) / acc.PEAK_BF16_MFMA
-        t_m = acc.problem_bytes(p) / acc.PEAK_HBM
-        if t_m > t_c:
-            return "hbm", acc.PEAK_HBM
-        return "mfma", acc.PEAK_BF16_MFMA
-    if kernel.startswith("mfma_f32"):
-        return "mfma", acc.PEAK_F32
-    return "alu", acc.PEAK_F32_VALU_UNPACKED
+        bound, peak = "mfma", acc.PEAK_BF16_MFMA
+    elif kernel.startswith("mfma_f32"):
+        bound, peak = "mfma", acc.PEAK_F32
+    else:
+        bound, peak = "alu", acc.PEAK_F32_VALU_UNPACKED
+    if acc.problem_bytes(p) / acc.PEAK_HBM > acc.problem_flops(p) / peak:
+        return "hbm", acc.PEAK_HBM
+    return bound, peak
 
 
 def time_workload(name, steps, warmup, **desc_overrides):
@@ -280,7 +281,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "copy"])
+    import workloads as W
+    ap.add_argument("--workload", default="c2", choices=list(W.WORKLOADS) + ["copy"])
     ap.add_argument("--secondary", default="c3",
                     help="second workload reported in the same line ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

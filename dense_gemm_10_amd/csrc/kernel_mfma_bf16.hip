@@ -93,11 +93,18 @@ __device__ __forceinline__ void dma_16(const void *base, uint32_t voff, uint32_t
 
 // 8 bf16 of one row at k = k_first .. k_first+7, zero for k >= ke (the
 // K-boundary mask of a partial K tile).  `row` points at k = 0 of the row;
-// ke >= 1.  Branch-free: the index is clamped to ke-1, so every load stays
-// inside the row, and masked elements are replaced by 0.
+// ke >= 1.  A chunk wholly inside the range is one 16-byte load (the row's
+// chunks are 16-byte aligned: lda is a multiple of 8 and the base
+// aligned), one wholly past it is zero without a load, and only the chunk
+// that straddles ke is read element by element (with the index clamped to
+// ke - 1, so every load stays inside the row).
 __device__ __forceinline__ uint4 load_chunk_tail(const uint16_t *row, int64_t k_first,
                                                  int64_t ke)
 {
+    if (k_first + 8 <= ke)
+        return *(const uint4 *)(row + k_first);
+    if (k_first >= ke)
+        return make_uint4(0u, 0u, 0u, 0u);
     uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {

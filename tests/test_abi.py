@@ -226,14 +226,15 @@ def test_stream_k_plan_for_a_badly_quantised_grid():
     d = _desc_for(W.WORKLOADS["c4"].replace(K=4096))
     ws = dg.dg_gemm_workspace_size(d)
     text = dg.dg_gemm_describe(d, ws)
-    assert "schedule=stream_k" in text and "bm=128 bn=128" in text
+    # with stream-K taking the tail wave the large tile is kept: 4095 x 4097
+    # in 256 x 256 tiles = 16 x 17 = 272 = one wave of 256 + 16 tail tiles
+    assert "schedule=stream_k" in text and "bm=256 bn=256" in text
     sk = _sk_fields(text)
-    # 4095 x 4097 in 128 x 128 tiles = 1056; one wave is 2 x 256 = 512
-    assert sk["dp_tiles"] == 1024 and sk["tail_tiles"] == 32
-    assert "fixup_blocks=%d " % (32 * 16) in text
+    assert sk["dp_tiles"] == 256 and sk["tail_tiles"] == 16
     assert sk["tail_splits"] == 16 and sk["tail_k_per_split"] == 256   # K = 4096
-    assert "programs=%d " % (1024 + 32 * 16) in text
-    assert ws == 32 * 16 * 128 * 128 * 4
+    assert "programs=%d " % (256 + 16 * 16) in text
+    assert "fixup_blocks=%d " % (16 * 64) in text
+    assert ws == 16 * 16 * 256 * 256 * 4
     # without workspace, or with K < 2048, the automatic choice stays data-parallel
     assert "schedule=data_parallel" in dg.dg_gemm_describe(d, 0)
     assert "schedule=data_parallel" in dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c4"]), 1 << 34)

@@ -129,3 +129,15 @@ def test_c4_no_activation_int_exact():
 def test_c5_batched_splitk(small_int):
     _full(W.WORKLOADS["c5"], small_int)
 
+
+
+# --- further shapes: flat K = 16 (HBM-bound) and a long-K ragged grid --------------
+@pytest.mark.parametrize("name", ["flat16", "flat16_f32"])
+@pytest.mark.parametrize("small_int", [False, True])
+def test_flat_small_k(name, small_int):
+    _full(W.WORKLOADS[name], small_int)
+
+
+@pytest.mark.parametrize("small_int", [False, True])
+def test_tail4352_sampled(small_int):
+    _sampled(W.WORKLOADS["tail4352"], n=2000, small_int=small_int)

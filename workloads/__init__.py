@@ -183,6 +183,29 @@ WORKLOADS = {
         stride_b=0,
         alpha=1.0, beta=0.0,
         dist_a=("normal", 1.0), dist_b=("normal", 1.0), seed=5),
+    # Shapes for the further steps.  The flat GEMM is the 4096 x 4096 x 16
+    # problem of "La GEMM, de zero a cuBLAS" (self-check questions): almost
+    # all of its bytes are the output, so it is bound by HBM writes; 2-byte
+    # elements as in that question's arithmetic, same layout as C3.  The
+    # long-K ragged shape is one where the last wave of 256 x 256 tiles is
+    # nearly empty (17 x 17 = 289 tiles on 256 compute units).
+    "flat16": Problem(
+        name="gemm_bf16_flat_4096x4096x16", M=4096, N=4096, K=16,
+        a_type=BF16, b_type=BF16, c_type=BF16,
+        a_order=ROW, b_order=COL, c_order=ROW,
+        alpha=1.0, beta=0.0,
+        dist_a=("normal", 1.0), dist_b=("normal", 1.0), seed=6),
+    "flat16_f32": Problem(
+        name="sgemm_f32_flat_4096x4096x16", M=4096, N=4096, K=16,
+        a_type=F32, b_type=F32, c_type=F32,
+        alpha=1.0, beta=0.0,
+        dist_a=("uniform", -1.0, 1.0), dist_b=("uniform", -1.0, 1.0), seed=7),
+    "tail4352": Problem(
+        name="gemm_bf16_4352x4352x8192", M=4352, N=4352, K=8192,
+        a_type=BF16, b_type=BF16, c_type=BF16,
+        a_order=ROW, b_order=COL, c_order=ROW,
+        alpha=1.0, beta=0.0,
+        dist_a=("normal", 1.0), dist_b=("normal", 1.0), seed=8),
 }
 
 
