@@ -9,7 +9,7 @@ with gcc and marshals arguments to it.
 Every function here is pinned by CPU tests against values fixed by the
 mathematics (exact integer and rational results, identity / permutation /
 rank-one closed forms, standard-normal table values for GELU, hand-worked
-bf16 rounding cases) rather than against itself.
+bf16 and fp16 rounding cases) rather than against itself.
 """
 from __future__ import annotations
 
@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-_DT = {"f32": 0, "bf16": 1}
+_DT = {"f32": 0, "bf16": 1, "f16": 2}
 _ACT = {"none": 0, "gelu_erf": 1, "gelu_tanh": 2}
 
 _lock = threading.Lock()
@@ -73,6 +73,10 @@ def _load():
             lib.oracle_gemm_points.restype = ctypes.c_int
             lib.oracle_round_bf16.argtypes = [ctypes.c_double]
             lib.oracle_round_bf16.restype = ctypes.c_uint16
+            lib.oracle_round_f16.argtypes = [ctypes.c_double]
+            lib.oracle_round_f16.restype = ctypes.c_uint16
+            lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
+            lib.oracle_f16_to_double.restype = ctypes.c_double
             lib.oracle_act.argtypes = [ctypes.c_double, ctypes.c_int32]
             lib.oracle_act.restype = ctypes.c_double
             lib.oracle_max_threads.restype = ctypes.c_int
@@ -107,11 +111,11 @@ def _out_dtype(p):
 def gemm(p, A, B, C, bias=None, nthreads=0):
     """Evaluate every output element.
 
-    A, B, C, bias are flat storage buffers (float32 or uint16 bf16 bits) laid
+    A, B, C, bias are flat storage buffers (float32, or uint16 bf16 / fp16 bits) laid
     out as ``p`` describes.  Returns (ref, mag, out), each dense
     [batch][M][N]: ref = the float64 result before output rounding,
     mag = |alpha| sum_k |a||b| + |beta||c| + |bias| (the error scale),
-    out = ref rounded to the output dtype (float32 or bf16 bits)."""
+    out = ref rounded to the output dtype (float32, or bf16 / fp16 bits)."""
     lib = _load()
     shape = (p.batch, p.M, p.N)
     ref = np.empty(shape, np.float64)
@@ -150,6 +154,16 @@ def round_bf16(x):
     return int(_load().oracle_round_bf16(float(x)))
 
 
+def round_f16(x):
+    """float64 -> IEEE binary16 bit pattern (round to nearest, ties to even)."""
+    return int(_load().oracle_round_f16(float(x)))
+
+
+def f16_to_float(bits):
+    """Decode one binary16 bit pattern to float64 (exact), as the oracle does."""
+    return float(_load().oracle_f16_to_double(int(bits)))
+
+
 def act(x, kind):
     return float(_load().oracle_act(float(x), _ACT[kind]))
 
@@ -162,3 +176,17 @@ def bf16_bits_to_float(bits):
     """Decode bf16 bit patterns (uint16 array) to float64 (exact)."""
     bits = np.asarray(bits, dtype=np.uint16)
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f16_bits_to_float(bits):
+    """Decode fp16 bit patterns (uint16 array) to float64 (exact)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def bits_to_float(bits, dtype):
+    """Decode a stored output buffer of dtype 'f32' / 'bf16' / 'f16' to float64."""
+    if dtype == "f32":
+        return np.asarray(bits, np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return bf16_bits_to_float(bits)
+    return f16_bits_to_float(bits)

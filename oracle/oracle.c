@@ -18,7 +18,10 @@
  *   - batch strides per operand, stride 0 broadcasting an operand ("Skill:
  *     Write a Triton GEMM Kernel", Correctness requirements);
  *   - the reference is computed on the CPU in float64 ("Skill: Write a
- *     Triton GEMM Kernel", Required reasoning process step 8).
+ *     Triton GEMM Kernel", Required reasoning process step 8);
+ *   - inputs in fp32, bf16 or fp16 ("Skill: Write a Triton GEMM Kernel",
+ *     Inputs the agent should gather first: input dtype), decoded exactly;
+ *     outputs rounded to nearest, ties to even, into fp32, bf16 or fp16.
  *
  * Readings where the pages are silent: the epilogue order is
  * act(alpha*acc + beta*c + bias); beta == 0 means C_in is not read;
@@ -41,6 +44,7 @@
 /* dtype codes used by this file's entry points */
 #define OR_F32 0
 #define OR_BF16 1
+#define OR_F16 2
 /* activation codes */
 #define OR_ACT_NONE 0
 #define OR_ACT_GELU_ERF 1
@@ -65,10 +69,33 @@ static double bf16_bits_to_double(uint16_t h)
     return (double)f;
 }
 
+/* ---- fp16 decode: IEEE 754 binary16, 1 sign bit, 5 exponent bits (bias
+ * 15), 10 fraction bits.  Exponent field 0 holds zero and the subnormals
+ * fraction * 2^-24; field 31 holds infinities and NaNs; otherwise the value
+ * is (1024 + fraction) * 2^(field - 25).  Every value is exact in double. */
+static double f16_bits_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int field = (h >> 10) & 0x1F;
+    int frac = h & 0x3FF;
+    double v;
+    if (field == 0)
+        v = ldexp((double)frac, -24);
+    else if (field == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + frac), field - 25);
+    return sign ? -v : v;
+}
+
+double oracle_f16_to_double(uint16_t h) { return f16_bits_to_double(h); }
+
 static double load_value(const void *base, int32_t type, int64_t idx)
 {
     if (type == OR_F32)
         return (double)((const float *)base)[idx];
+    if (type == OR_F16)
+        return f16_bits_to_double(((const uint16_t *)base)[idx]);
     return bf16_bits_to_double(((const uint16_t *)base)[idx]);
 }
 
@@ -114,6 +141,49 @@ uint16_t oracle_round_bf16(double x)
     uint32_t u;
     memcpy(&u, &pf, sizeof u);
     return (uint16_t)(sign | (uint16_t)(u >> 16));
+}
+
+/* ---- fp16 encode: round a double to the nearest binary16, ties to even --
+ * Normal numbers in [2^e, 2^(e+1)), e >= -14, are spaced 2^(e-10) apart;
+ * below 2^-14 (subnormals) the spacing is 2^-24.  As for bf16, the nearer
+ * of the two neighbours lo <= |x| < lo + spacing wins and a tie goes to the
+ * even significand.  The largest finite value is (2 - 2^-10) * 2^15 =
+ * 65504; at or above the midpoint 65520 between it and 2^16 the result is
+ * infinity.  NaN becomes the quiet NaN 0x7E00 with its sign. */
+uint16_t oracle_round_f16(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7E00u);
+    double ax = fabs(x);
+    if (ax >= 65520.0)
+        return (uint16_t)(sign | 0x7C00u);
+    if (ax == 0.0)
+        return sign;
+    int e;
+    (void)frexp(ax, &e);            /* ax in [2^(e-1), 2^e) */
+    int exp_unbiased = e - 1;
+    if (exp_unbiased < -14)
+        exp_unbiased = -14;         /* subnormal range shares the 2^-24 spacing */
+    double spacing = ldexp(1.0, exp_unbiased - 10);
+    double q = floor(ax / spacing); /* exact: division by a power of two */
+    double lo = q * spacing;
+    double hi = lo + spacing;
+    double dlo = ax - lo, dhi = hi - ax;
+    double pick;
+    if (dlo < dhi)
+        pick = lo;
+    else if (dhi < dlo)
+        pick = hi;
+    else
+        pick = (fmod(q, 2.0) == 0.0) ? lo : hi;
+    /* encode the (exactly representable) pick */
+    if (pick < ldexp(1.0, -14))                       /* zero or subnormal */
+        return (uint16_t)(sign | (uint16_t)(pick / ldexp(1.0, -24)));
+    (void)frexp(pick, &e);
+    int E = e - 1;                                    /* pick in [2^E, 2^(E+1)) */
+    uint16_t frac = (uint16_t)((pick / ldexp(1.0, E) - 1.0) * 1024.0);
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | frac);
 }
 
 /* ---- activation --------------------------------------------------------
@@ -164,6 +234,8 @@ static void one_element(const oracle_problem *p, const void *A, const void *B,
     mag[out_idx] = fabs(p->alpha) * amag + fabs(p->beta) * fabs(c) + fabs(bj);
     if (p->c_type == OR_F32)
         ((float *)out)[out_idx] = (float)v;
+    else if (p->c_type == OR_F16)
+        ((uint16_t *)out)[out_idx] = oracle_round_f16(v);
     else
         ((uint16_t *)out)[out_idx] = oracle_round_bf16(v);
 }

@@ -4,7 +4,7 @@ None of these compares the oracle with itself: expected values come from
 exact integer / rational arithmetic written independently here, closed forms
 (identity, permutation, rank one, alpha = 0, beta = 0), an independent
 library product (numpy float64 matmul), textbook standard-normal values and
-hand-worked bf16 rounding cases.  A dropped term, a wrong sign, a transposed
+hand-worked bf16 and fp16 rounding cases.  A dropped term, a wrong sign, a transposed
 operand or a wrong layout index in the oracle fails at least one of them.
 """
 import itertools
@@ -22,9 +22,11 @@ ORDERS = [W.ROW, W.COL]
 
 
 def _log_f64(x, dtype):
-    """Storage values -> float64 (bf16 decoded exactly)."""
+    """Storage values -> float64 (bf16 / fp16 decoded exactly)."""
     if dtype == W.BF16:
         return oracle.bf16_bits_to_float(x)
+    if dtype == W.F16:
+        return oracle.f16_bits_to_float(x)
     return x.astype(np.float64)
 
 
@@ -37,7 +39,7 @@ def _run(p, x):
 # ---------------------------------------------------------------------------
 INT_CASES = []
 for (ta, tc), (ao, bo, co) in itertools.product(
-        [(W.F32, W.F32), (W.BF16, W.BF16), (W.BF16, W.F32)],
+        [(W.F32, W.F32), (W.BF16, W.BF16), (W.BF16, W.F32), (W.F16, W.F16), (W.F16, W.F32)],
         itertools.product(ORDERS, ORDERS, ORDERS)):
     INT_CASES.append((ta, tc, ao, bo, co))
 
@@ -69,8 +71,8 @@ def test_p1_small_integer_exact(ta, tc, ao, bo, co):
                 assert np.array_equal(out[b].astype(np.float64) * 2, twice.astype(np.float64))
             else:
                 # |2 out| <= 3*4*17 + 2 + 4 < 256: every half-integer result
-                # has at most 8 significant bits, so bf16 holds it exactly.
-                assert np.array_equal(oracle.bf16_bits_to_float(out[b]) * 2, twice.astype(np.float64))
+                # has at most 8 significant bits, so bf16 (and fp16) holds it exactly.
+                assert np.array_equal(_log_f64(out[b], tc) * 2, twice.astype(np.float64))
 
 
 def test_p1_integer_larger_k_f32():
@@ -350,3 +352,93 @@ def test_p9_bf16_output_rounding_in_gemm():
     ref, mag, out = oracle.gemm(p, A, B, C)
     assert ref[0, 0, 0] == 1.0 + 2 ** -8
     assert out[0, 0, 0] == 0x3F80
+
+
+# ---------------------------------------------------------------------------
+# P10: fp16 inputs and output ("Skill: Write a Triton GEMM Kernel", Inputs the
+# agent should gather first: input dtype; fp16 is the dtype of the pages'
+# allclose check)
+# ---------------------------------------------------------------------------
+def test_p10_f16_rne_table():
+    rows = read_golden("f16_rne.txt")
+    assert len(rows) >= 25
+    for row in rows:
+        x, expect = _parse_float(row[0]), int(row[1], 16)
+        assert oracle.round_f16(x) == expect, (row[0], hex(oracle.round_f16(x)), row[1])
+
+
+def test_p10_f16_rne_matches_numpy_on_random_doubles():
+    # numpy's float64 -> float16 conversion rounds to nearest even straight
+    # from double (one rounding): an independent implementation of the format
+    rng = np.random.default_rng(5)
+    xs = np.concatenate([
+        rng.standard_normal(4000) * 10.0 ** rng.integers(-9, 6, 4000),
+        rng.uniform(-70000, 70000, 500),
+        # every midpoint between adjacent fp16 values of one binade, and next to it
+        (np.arange(1024, 2048) + 0.5) * 2.0 ** -10,
+        np.nextafter((np.arange(1024, 2048) + 0.5) * 2.0 ** -10, 0),
+        (np.arange(0, 1024) + 0.5) * 2.0 ** -24,
+    ])
+    want = xs.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.round_f16(x) for x in xs], np.uint16)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, [(float.hex(float(xs[i])), hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+def test_p10_f16_decode_every_pattern():
+    # every finite bit pattern, decoded through numpy's float16 as the
+    # independent route; NaN patterns decode to NaN, infinities keep their sign
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    want = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_float(b) for b in bits[::7]])
+    w = want[::7]
+    same = (got == w) | (np.isnan(got) & np.isnan(w))
+    assert same.all()
+    assert oracle.f16_to_float(0x0001) == 2.0 ** -24
+    assert oracle.f16_to_float(0x7BFF) == 65504.0
+    assert oracle.f16_to_float(0xFC00) == -math.inf
+
+
+def test_p10_f16_inputs_decoded_exactly():
+    p = W.Problem(name="h", M=31, N=29, K=37, a_type=W.F16, b_type=W.F16, c_type=W.F32,
+                  a_order=W.ROW, b_order=W.COL, dist_a=("normal", 1.0), dist_b=("normal", 1.0),
+                  alpha=1.0, beta=0.0, seed=23)
+    x = W.make_inputs(p)
+    ref, mag, out = _run(p, x)
+    # decode by an independent route: expand each half to float32 by
+    # rebuilding sign, exponent and fraction with integer arithmetic
+    def expand(h):
+        h = h.astype(np.int64)
+        sign = np.where(h >> 15, -1.0, 1.0)
+        e = (h >> 10) & 31
+        f = h & 1023
+        return sign * np.where(e == 0, f * 2.0 ** -24, (1024 + f) * 2.0 ** (e - 25))
+    A = expand(x.A_log.reshape(p.M, p.K))
+    B = expand(x.B_log.reshape(p.K, p.N))
+    assert np.all(np.abs(ref[0] - A @ B) <= 1e-13 * mag[0])
+
+
+def test_p10_f16_output_rounding_in_gemm():
+    # 1 * 1 + 2^-11 * 1 is the tie between 1 and 1 + 2^-10: even (1.0) wins;
+    # 1 + 2^-10 + 2^-11 ties between odd 1 + 2^-10 and even 1 + 2^-9
+    p = W.Problem(name="tie", M=1, N=2, K=3, a_type=W.F16, b_type=W.F16, c_type=W.F16,
+                  b_order=W.COL)
+    A = np.array([0x3C00, 0x1000, 0x1400], np.uint16)     # 1, 2^-11, 2^-10
+    B = np.array([0x3C00, 0x3C00, 0x0000,                  # column 0: 1, 1, 0
+                  0x3C00, 0x3C00, 0x3C00], np.uint16)      # column 1: 1, 1, 1
+    C = np.zeros(2, np.uint16)
+    ref, mag, out = oracle.gemm(p, A, B, C)
+    assert ref[0, 0, 0] == 1.0 + 2 ** -11 and out[0, 0, 0] == 0x3C00
+    assert ref[0, 0, 1] == 1.0 + 2 ** -10 + 2 ** -11 and out[0, 0, 1] == 0x3C02
+
+
+def test_p10_f16_overflow_to_infinity_in_gemm():
+    # 255 * 255 + 255 * 2 = 65535 is above the 65520 midpoint: +inf; with
+    # alpha = -1 the sign follows
+    p = W.Problem(name="ovf", M=1, N=1, K=2, a_type=W.F16, b_type=W.F16, c_type=W.F16)
+    A = np.array([0x5BF8, 0x5BF8], np.uint16)   # 255, 255
+    B = np.array([0x5BF8, 0x4000], np.uint16)   # 255, 2
+    ref, mag, out = oracle.gemm(p, A, B, np.zeros(1, np.uint16))
+    assert ref[0, 0, 0] == 65535.0 and out[0, 0, 0] == 0x7C00
+    ref, mag, out = oracle.gemm(p.replace(alpha=-1.0), A, B, np.zeros(1, np.uint16))
+    assert out[0, 0, 0] == 0xFC00

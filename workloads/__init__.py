@@ -3,7 +3,7 @@
 This module is shared by the CPU oracle side (tests, cpu baseline) and the
 GPU side (tests, bench).  It holds no GEMM arithmetic: it only draws random
 numbers, converts them to the storage dtype with a library cast (torch's CPU
-fp32 -> bfloat16 cast, round-to-nearest-even) and lays the logical matrices
+fp32 -> bfloat16 / float16 casts, round-to-nearest-even) and lays the logical matrices
 out in memory with the requested order, leading dimension and batch stride.
 
 The problem statement is the one of "La GEMM, de zero a cuBLAS" section 2.1
@@ -15,7 +15,7 @@ Seeds: operand ``o`` of workload ``w`` is drawn from
 ``numpy.random.default_rng([w, o])`` with o = 0 (A), 1 (B), 2 (C_in), 3 (bias).
 Uniform U(a, b) is drawn in fp64 and cast to fp32; normal N(0, s) is
 ``standard_normal * s`` cast to fp32 (s is the standard deviation).  bf16
-operands are the RNE rounding of those fp32 values.  The "small integer twin"
+and fp16 operands are the RNE rounding of those fp32 values.  The "small integer twin"
 of a workload draws every operand from {-2, ..., 2} instead.
 """
 from __future__ import annotations
@@ -27,6 +27,7 @@ import numpy as np
 
 F32 = "f32"
 BF16 = "bf16"
+F16 = "f16"
 ROW = "row"
 COL = "col"
 
@@ -34,7 +35,7 @@ ACT_NONE = "none"
 ACT_GELU_ERF = "gelu_erf"
 ACT_GELU_TANH = "gelu_tanh"
 
-_ELEM_BYTES = {F32: 4, BF16: 2}
+_ELEM_BYTES = {F32: 4, BF16: 2, F16: 2}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -224,14 +225,15 @@ def _draw(rng, dist, n, small_int):
 
 
 def to_storage(values_f32, dtype):
-    """fp32 values -> storage array (float32, or uint16 bf16 bit patterns).
+    """fp32 values -> storage array (float32, or uint16 bf16 / fp16 bit
+    patterns).
 
-    bf16 uses torch's CPU cast (round to nearest, ties to even)."""
+    bf16 and fp16 use torch's CPU casts (round to nearest, ties to even)."""
     values_f32 = np.ascontiguousarray(values_f32, dtype=np.float32)
     if dtype == F32:
         return values_f32
     import torch
-    t = torch.from_numpy(values_f32).to(torch.bfloat16)
+    t = torch.from_numpy(values_f32).to(torch.bfloat16 if dtype == BF16 else torch.float16)
     return t.view(torch.int16).numpy().view(np.uint16).copy()
 
 
@@ -244,10 +246,10 @@ def _fill_value(dtype, fill):
         return 0
     if dtype == F32:
         return np.float32(fill)
-    # bf16 sentinels as bit patterns
+    # 16-bit sentinels as bit patterns (a NaN with a payload)
     if isinstance(fill, float) and np.isnan(fill):
-        return np.uint16(0x7FC1)
-    return to_storage(np.array([fill], np.float32), BF16)[0]
+        return np.uint16(0x7FC1 if dtype == BF16 else 0x7E01)
+    return to_storage(np.array([fill], np.float32), dtype)[0]
 
 
 def _strided_view(buf, order, ld, base, rows, cols):

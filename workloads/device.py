@@ -4,11 +4,11 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import BF16, Problem, desc_fields
+from . import F32, Problem, desc_fields
 
 
 def to_device(arr, device="cuda"):
-    """Host storage array (float32 or uint16 bf16 bits) -> device tensor with
+    """Host storage array (float32, or uint16 bf16 / fp16 bits) -> device tensor with
     the same bytes."""
     import torch
     if arr is None:
@@ -25,7 +25,7 @@ def to_device(arr, device="cuda"):
 def to_host(t, dtype):
     """Device tensor -> host numpy array in storage dtype."""
     a = t.cpu().numpy()
-    return a.view(np.uint16) if dtype == BF16 else a
+    return a if dtype == F32 else a.view(np.uint16)
 
 
 class DeviceProblem:
