@@ -38,7 +38,7 @@ def log(*a):
 
 
 def _dtype_name(p):
-    return "f32" if p.a_type == "f32" else "bf16"
+    return p.a_type
 
 
 def _roofline_peak(p, kernel):
@@ -49,6 +49,8 @@ def _roofline_peak(p, kernel):
     from dense_gemm_10_amd import accounting as acc
     if kernel.startswith("mfma_bf16"):
         bound, peak = "mfma", acc.PEAK_BF16_MFMA
+    elif kernel.startswith("mfma_f16"):
+        bound, peak = "mfma", acc.PEAK_F16_MFMA
     elif kernel.startswith("mfma_f32"):
         bound, peak = "mfma", acc.PEAK_F32
     else:

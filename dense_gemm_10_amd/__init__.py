@@ -17,10 +17,10 @@ import os
 import threading
 
 __all__ = [
-    "DG_F32", "DG_BF16", "DG_ROW_MAJOR", "DG_COL_MAJOR",
+    "DG_F32", "DG_BF16", "DG_F16", "DG_ROW_MAJOR", "DG_COL_MAJOR",
     "DG_ACT_NONE", "DG_ACT_GELU_ERF", "DG_ACT_GELU_TANH",
     "DG_ALGO_AUTO", "DG_ALGO_GENERIC", "DG_ALGO_VALU_F32", "DG_ALGO_MFMA_BF16",
-    "DG_ALGO_MFMA_F32", "DgGemmDesc", "DgError", "make_desc", "dg_version",
+    "DG_ALGO_MFMA_F32", "DG_ALGO_MFMA_F16", "DgGemmDesc", "DgError", "make_desc", "dg_version",
     "dg_status_string", "dg_gemm_workspace_size", "dg_gemm", "dg_gemm_describe",
     "dg_schedule_map", "gemm", "library_path",
 ]
@@ -35,13 +35,14 @@ DG_ERROR_NOT_SUPPORTED = 2
 DG_ERROR_INSUFFICIENT_WORKSPACE = 3
 DG_ERROR_LAUNCH = 4
 # enums
-DG_F32, DG_BF16 = 0, 1
+DG_F32, DG_BF16, DG_F16 = 0, 1, 2
 DG_ROW_MAJOR, DG_COL_MAJOR = 0, 1
 DG_ACT_NONE, DG_ACT_GELU_ERF, DG_ACT_GELU_TANH = 0, 1, 2
-DG_ALGO_AUTO, DG_ALGO_GENERIC, DG_ALGO_VALU_F32, DG_ALGO_MFMA_BF16, DG_ALGO_MFMA_F32 = range(5)
+(DG_ALGO_AUTO, DG_ALGO_GENERIC, DG_ALGO_VALU_F32, DG_ALGO_MFMA_BF16, DG_ALGO_MFMA_F32,
+ DG_ALGO_MFMA_F16) = range(6)
 DG_SCHED_AUTO, DG_SCHED_DATA_PARALLEL, DG_SCHED_STREAM_K = range(3)
 
-_DTYPE = {"f32": DG_F32, "bf16": DG_BF16}
+_DTYPE = {"f32": DG_F32, "bf16": DG_BF16, "f16": DG_F16}
 _ORDER = {"row": DG_ROW_MAJOR, "col": DG_COL_MAJOR}
 _ACT = {"none": DG_ACT_NONE, "gelu_erf": DG_ACT_GELU_ERF, "gelu_tanh": DG_ACT_GELU_TANH}
 
@@ -206,6 +207,8 @@ def _torch_dtype_name(t):
         return "f32"
     if t.dtype == torch.bfloat16:
         return "bf16"
+    if t.dtype == torch.float16:
+        return "f16"
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 

@@ -8,7 +8,7 @@ Throughput is reported as TFLOPS = 2MNK / t ("GEMM Kernel Optimization",
 Verification).
 
 MI355X peaks (AMD's published figures, dense, no sparsity):
-  - bf16 MFMA 2516.6 TFLOP/s, fp32 (vector and matrix) 157.3 TFLOP/s,
+  - bf16 and fp16 MFMA 2516.6 TFLOP/s, fp32 (vector and matrix) 157.3 TFLOP/s,
     HBM3E 8 TB/s; 256 compute units at 2.4 GHz.
   - FP32 vector without packed-FP32 instructions: each of the 4 SIMDs of a
     CU retires 16 fp32 FMA lanes per clock, i.e. 64 FMA = 128 flop per clock
@@ -21,11 +21,12 @@ from __future__ import annotations
 N_CU = 256
 CLOCK_HZ = 2.4e9
 PEAK_BF16_MFMA = 2516.6e12          # 256 CU * 4096 flop/clk * 2.4 GHz
+PEAK_F16_MFMA = 2516.6e12           # same rate for fp16 inputs
 PEAK_F32 = 157.3e12                 # published fp32 vector / matrix peak
 PEAK_F32_VALU_UNPACKED = N_CU * 128 * CLOCK_HZ   # 78.64e12
 PEAK_HBM = 8.0e12                   # bytes / s
 
-_ELEM = {"f32": 4, "bf16": 2}
+_ELEM = {"f32": 4, "bf16": 2, "f16": 2}
 
 
 def flops(M, N, K, batch=1):
@@ -87,4 +88,6 @@ def compute_peak_for(p):
     """The compute peak that bounds a workload's inner loop on MI355X."""
     if p.a_type == "bf16":
         return PEAK_BF16_MFMA
+    if p.a_type == "f16":
+        return PEAK_F16_MFMA
     return PEAK_F32

@@ -31,7 +31,7 @@ SOURCES = [
     "api.cpp",
     "kernel_generic.hip",
     "kernel_valu_f32.hip",
-    "kernel_mfma_bf16.hip",
+    "kernel_mfma16.hip",
     "kernel_mfma_f32.hip",
 ]
 

@@ -19,13 +19,16 @@
 
 using namespace dg;
 
+static_assert(DT_F32 == DG_F32 && DT_BF16 == DG_BF16 && DT_F16 == DG_F16,
+              "kernel dtype codes follow dg_dtype");
+
 namespace {
 
 constexpr int64_t kNumCu = 256;          // MI355X compute units
 constexpr int32_t kDefaultGroupM = 8;    // "GEMM Kernel Optimization", L2 Cache Grouping
 constexpr int32_t kMaxSplits = 256;
 
-int64_t elem_size(int32_t t) { return t == DG_BF16 ? 2 : 4; }
+int64_t elem_size(int32_t t) { return t == DG_F32 ? 4 : 2; }
 
 bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
 bool add_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_add_overflow(a, b, out); }
@@ -79,7 +82,7 @@ dg_status validate_desc(const dg_gemm_desc *d, Extents *ext)
         return DG_ERROR_INVALID_VALUE;
     if (d->M < 0 || d->N < 0 || d->K < 0 || d->batch < 0)
         return DG_ERROR_INVALID_VALUE;
-    auto dtype_ok = [](int32_t t) { return t == DG_F32 || t == DG_BF16; };
+    auto dtype_ok = [](int32_t t) { return t == DG_F32 || t == DG_BF16 || t == DG_F16; };
     auto order_ok = [](int32_t o) { return o == DG_ROW_MAJOR || o == DG_COL_MAJOR; };
     if (!dtype_ok(d->a_type) || !dtype_ok(d->b_type) || !dtype_ok(d->c_type))
         return DG_ERROR_INVALID_VALUE;
@@ -87,7 +90,7 @@ dg_status validate_desc(const dg_gemm_desc *d, Extents *ext)
         return DG_ERROR_INVALID_VALUE;
     if (d->act < DG_ACT_NONE || d->act > DG_ACT_GELU_TANH)
         return DG_ERROR_INVALID_VALUE;
-    if (d->algo < DG_ALGO_AUTO || d->algo > DG_ALGO_MFMA_F32)
+    if (d->algo < DG_ALGO_AUTO || d->algo > DG_ALGO_MFMA_F16)
         return DG_ERROR_INVALID_VALUE;
     if (d->split_k < 0 || d->group_m < 0 || d->xcd_remap < -1 || d->xcd_remap > 1)
         return DG_ERROR_INVALID_VALUE;
@@ -106,7 +109,8 @@ dg_status validate_desc(const dg_gemm_desc *d, Extents *ext)
         return DG_ERROR_INVALID_VALUE;
     if (d->ldc < (d->c_order == DG_ROW_MAJOR ? d->N : d->M))
         return DG_ERROR_INVALID_VALUE;
-    // supported dtype combinations
+    // supported dtype combinations: A and B of one type; fp32 inputs give
+    // an fp32 output, 16-bit inputs any output type
     if (d->a_type != d->b_type)
         return DG_ERROR_NOT_SUPPORTED;
     if (d->a_type == DG_F32 && d->c_type != DG_F32)
@@ -183,9 +187,10 @@ bool valu_eligible(const dg_gemm_desc *d, const void *A, const void *B)
            strides_aligned(d, 4);
 }
 
-bool mfma_bf16_eligible(const dg_gemm_desc *d, const void *A, const void *B)
+// bf16 or fp16 (`type`) matrix-core kernel
+bool mfma16_eligible(const dg_gemm_desc *d, int32_t type, const void *A, const void *B)
 {
-    if (d->a_type != DG_BF16 || d->a_order != DG_ROW_MAJOR || d->b_order != DG_COL_MAJOR)
+    if (d->a_type != type || d->a_order != DG_ROW_MAJOR || d->b_order != DG_COL_MAJOR)
         return false;
     // the kernel addresses a tile with 32-bit byte offsets: 256 rows * ld * 2 < 2^31
     return aligned_to(A, 16) && aligned_to(B, 16) && d->lda % 8 == 0 && d->ldb % 8 == 0 &&
@@ -237,10 +242,6 @@ TileConfig pick_quantised(const dg_gemm_desc *d, const TileConfig *table, int n)
     return t128;
 }
 
-TileConfig pick_mfma_tile(const dg_gemm_desc *d)
-{
-    return pick_quantised(d, kMfmaBf16Tiles, kNumMfmaBf16Tiles);
-}
 
 // Split-K slices for `tiles` output tiles: only when the tiles alone leave
 // most compute units idle and every slice keeps a long K range.
@@ -294,7 +295,7 @@ dg_status finish_plan(const dg_gemm_desc *d, Plan p, size_t ws_avail, bool ws_kn
 
     // Stream-K ("La GEMM, de zero a cuBLAS", section 2.10: split the work
     // along K so that the last wave is not left mostly idle), for the bf16
-    // matrix-core kernel on one matrix without split-K.  The tiles of the
+    // and fp16 matrix-core kernels on one matrix without split-K.  The tiles of the
     // full waves stay data-parallel; each of the R tail tiles is cut into S
     // K slices, S about wave / R, so the tail fills one more wave.  Only
     // when the tail wave would be less than 85 % full, every slice keeps at
@@ -303,8 +304,8 @@ dg_status finish_plan(const dg_gemm_desc *d, Plan p, size_t ws_avail, bool ws_kn
     // a shorter K the tail tiles' epilogues cost about as much as their K
     // loop and slicing them gained nothing in measurements (4095 x 4097 x
     // 1000: 101 vs 103 us with GELU, 91 vs 85 us without).
-    const bool sk_possible = p.kernel == KERNEL_MFMA_BF16 && d->batch == 1 && S == 1 &&
-                             reads_ab(d) && p.tile.per_cu > 0;
+    const bool sk_possible = (p.kernel == KERNEL_MFMA_BF16 || p.kernel == KERNEL_MFMA_F16) &&
+                             d->batch == 1 && S == 1 && reads_ab(d) && p.tile.per_cu > 0;
     if (d->schedule == DG_SCHED_STREAM_K && !sk_possible)
         return DG_ERROR_NOT_SUPPORTED;
     if (sk_possible && d->schedule != DG_SCHED_DATA_PARALLEL) {
@@ -342,11 +343,23 @@ dg_status make_plan(const dg_gemm_desc *d, const void *A, const void *B, size_t 
 {
     Plan p{};
     const int32_t algo = d->algo;
-    if (algo == DG_ALGO_MFMA_BF16 || (algo == DG_ALGO_AUTO && mfma_bf16_eligible(d, A, B))) {
-        if (!mfma_bf16_eligible(d, A, B))
+    const TileConfig *table16 = nullptr;   // tiles of the 16-bit matrix-core kernel
+    int n16 = 0;
+    if (algo == DG_ALGO_MFMA_BF16 || (algo == DG_ALGO_AUTO && mfma16_eligible(d, DG_BF16, A, B))) {
+        if (!mfma16_eligible(d, DG_BF16, A, B))
             return DG_ERROR_NOT_SUPPORTED;
         p.kernel = KERNEL_MFMA_BF16;
-        p.tile = pick_mfma_tile(d);
+        table16 = kMfmaBf16Tiles;
+        n16 = kNumMfmaBf16Tiles;
+        p.tile = pick_quantised(d, table16, n16);
+    } else if (algo == DG_ALGO_MFMA_F16 ||
+               (algo == DG_ALGO_AUTO && mfma16_eligible(d, DG_F16, A, B))) {
+        if (!mfma16_eligible(d, DG_F16, A, B))
+            return DG_ERROR_NOT_SUPPORTED;
+        p.kernel = KERNEL_MFMA_F16;
+        table16 = kMfmaF16Tiles;
+        n16 = kNumMfmaF16Tiles;
+        p.tile = pick_quantised(d, table16, n16);
     } else if (algo == DG_ALGO_MFMA_F32 || (algo == DG_ALGO_AUTO && valu_eligible(d, A, B))) {
         // fp32 on the matrix cores: same operand requirements as the VALU kernel
         if (!valu_eligible(d, A, B))
@@ -362,15 +375,14 @@ dg_status make_plan(const dg_gemm_desc *d, const void *A, const void *B, size_t 
         p.kernel = KERNEL_GENERIC;
         p.tile = kGenericTiles[0];
     }
-    // The bf16 choice above falls back to the small tile when the large
+    // The 16-bit choice above falls back to the small tile when the large
     // one leaves a nearly empty last wave.  When stream-K takes that tail
     // wave instead (automatic choice, workspace given), the large tile with
-    // its better flop-per-byte ratio wins: 4352 x 4352 x 8192 ran 295 us
-    // that way against 415 us on 128 x 128 tiles.
-    if (p.kernel == KERNEL_MFMA_BF16 && !forced_tile(kMfmaBf16Tiles, kNumMfmaBf16Tiles) &&
-        p.tile.bm != kMfmaBf16Tiles[0].bm) {
+    // its better flop-per-byte ratio wins: 4352 x 4352 x 8192 (bf16) ran
+    // 295 us that way against 415 us on 128 x 128 tiles.
+    if (table16 && !forced_tile(table16, n16) && p.tile.bm != table16[0].bm) {
         Plan big = p;
-        big.tile = kMfmaBf16Tiles[0];
+        big.tile = table16[0];
         Plan done;
         if (finish_plan(d, big, ws_avail, ws_known, &done) == DG_SUCCESS && done.sk.tail_tiles > 0) {
             *plan = done;
@@ -404,11 +416,11 @@ void fill_args(const dg_gemm_desc *d, const Plan &p, const void *A, const void *
     g->a_col = d->a_order == DG_COL_MAJOR;
     g->b_col = d->b_order == DG_COL_MAJOR;
     g->c_col = d->c_order == DG_COL_MAJOR;
-    g->c_bf16 = d->c_type == DG_BF16;
-    g->bias_bf16 = d->bias_type == DG_BF16;
+    g->c_type = d->c_type;
+    g->bias_type = d->bias_type;
     g->act = d->act;
     g->write_partial = p.splits > 1;
-    g->ab_bf16 = d->a_type == DG_BF16;
+    g->ab_type = d->a_type;
     g->sched.num_pid_m = ceil_div(d->M, p.tile.bm);
     g->sched.num_pid_n = ceil_div(d->N, p.tile.bn);
     g->sched.batch = d->batch;
@@ -426,6 +438,7 @@ const char *kernel_name(Kernel k)
     case KERNEL_VALU_F32: return "valu_f32";
     case KERNEL_MFMA_BF16: return "mfma_bf16";
     case KERNEL_MFMA_F32: return "mfma_f32";
+    case KERNEL_MFMA_F16: return "mfma_f16";
     }
     return "?";
 }
@@ -532,7 +545,8 @@ dg_status dg_gemm(const dg_gemm_desc *d, const void *A, const void *B, void *C, 
     switch (p.kernel) {
     case KERNEL_GENERIC: err = launch_generic(g, p, s); break;
     case KERNEL_VALU_F32: err = launch_valu_f32(g, p, s); break;
-    case KERNEL_MFMA_BF16: err = launch_mfma_bf16(g, p, s); break;
+    case KERNEL_MFMA_BF16:
+    case KERNEL_MFMA_F16: err = launch_mfma16(g, p, s); break;
     case KERNEL_MFMA_F32: err = launch_mfma_f32(g, p, s); break;
     default: return DG_ERROR_NOT_SUPPORTED;
     }

@@ -1,6 +1,6 @@
 // Device-side building blocks shared by the GEMM kernels: the kernel
 // argument block, typed element access with per-operand order / leading
-// dimension / batch stride, bf16 conversion and the fused epilogue.
+// dimension / batch stride, bf16 / fp16 conversion and the fused epilogue.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -22,19 +22,21 @@ struct GemmArgs {
     int64_t k_per_split;       // K range of one split (multiple of the kernel's BK)
     float alpha, beta;
     int32_t a_col, b_col, c_col;   // 1 = column-major
-    int32_t c_bf16;                // output dtype: 1 = bf16, 0 = fp32
-    int32_t bias_bf16;
+    int32_t c_type;                // output dtype (DT_*)
+    int32_t bias_type;             // bias dtype (DT_*)
     int32_t act;                   // dg_act
     int32_t write_partial;         // 1: store raw fp32 partials to ws, no epilogue
-    int32_t ab_bf16;               // input dtype of A and B: 1 = bf16, 0 = fp32
+    int32_t ab_type;               // dtype of A and B (DT_*)
     SchedArgs sched;
     StreamK sk;                    // sk.tail_tiles == 0: data-parallel launch
     float *sk_parts;               // stream-K partials, [tail tile][slice][BM * BN] fp32
 };
 
 enum { ACT_NONE = 0, ACT_GELU_ERF = 1, ACT_GELU_TANH = 2 };
+// element types, numbered as dg_dtype
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 
-// ---- bf16 <-> fp32 ---------------------------------------------------------
+// ---- 16-bit floats <-> fp32 -----------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint16_t h)
 {
     return __uint_as_float(((uint32_t)h) << 16);
@@ -47,6 +49,31 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x)
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// IEEE binary16: exact widening; narrowing rounds to nearest, ties to even
+// (hardware conversion), beyond the largest finite value to infinity.
+__device__ __forceinline__ float f16_to_f32(uint16_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16(float x)
+{
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// One 16-bit element of type T (DT_BF16 or DT_F16) <-> fp32.
+template <int T>
+__device__ __forceinline__ float half_to_f32(uint16_t h)
+{
+    return T == DT_F16 ? f16_to_f32(h) : bf16_to_f32(h);
+}
+
+template <int T>
+__device__ __forceinline__ uint16_t f32_to_half(float x)
+{
+    return T == DT_F16 ? f32_to_f16(x) : f32_to_bf16(x);
+}
+
 // ---- typed loads -------------------------------------------------------------
 __device__ __forceinline__ int64_t elem_offset(int32_t col_major, int64_t ld, int64_t r,
                                                int64_t c)
@@ -54,9 +81,12 @@ __device__ __forceinline__ int64_t elem_offset(int32_t col_major, int64_t ld, in
     return col_major ? c * ld + r : r * ld + c;
 }
 
-__device__ __forceinline__ float load_as_f32(const void *base, int32_t is_bf16, int64_t idx)
+__device__ __forceinline__ float load_as_f32(const void *base, int32_t type, int64_t idx)
 {
-    return is_bf16 ? bf16_to_f32(((const uint16_t *)base)[idx]) : ((const float *)base)[idx];
+    if (type == DT_F32)
+        return ((const float *)base)[idx];
+    const uint16_t h = ((const uint16_t *)base)[idx];
+    return type == DT_F16 ? f16_to_f32(h) : bf16_to_f32(h);
 }
 
 // ---- activation ------------------------------------------------------------
@@ -112,10 +142,10 @@ __device__ __forceinline__ float epilogue_value(const GemmArgs &g, int64_t b, in
     float v = g.alpha * acc;
     if (g.beta != 0.0f) {
         int64_t ci = b * g.sc + elem_offset(g.c_col, g.ldc, m, n);
-        v = fmaf(g.beta, load_as_f32(g.C, g.c_bf16, ci), v);
+        v = fmaf(g.beta, load_as_f32(g.C, g.c_type, ci), v);
     }
     if (g.bias)
-        v += load_as_f32(g.bias, g.bias_bf16, n);
+        v += load_as_f32(g.bias, g.bias_type, n);
     return activate(v, g.act);
 }
 
@@ -123,8 +153,10 @@ __device__ __forceinline__ void store_c(const GemmArgs &g, int64_t b, int64_t m,
                                         float v)
 {
     int64_t ci = b * g.sc + elem_offset(g.c_col, g.ldc, m, n);
-    if (g.c_bf16)
+    if (g.c_type == DT_BF16)
         ((uint16_t *)g.C)[ci] = f32_to_bf16(v);
+    else if (g.c_type == DT_F16)
+        ((uint16_t *)g.C)[ci] = f32_to_f16(v);
     else
         ((float *)g.C)[ci] = v;
 }

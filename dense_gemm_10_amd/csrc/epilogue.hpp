@@ -27,11 +27,6 @@ __device__ __forceinline__ void lds_barrier()
 // dimension: v = act(alpha*acc + beta*C + bias).  `go` is the line (row of
 // a row-major C, column of a column-major one), `gi` the first element of
 // the run along the line, `lim` the line length; elements past lim are
-// left untouched.  The branches on beta / bias / act are uniform.
-// Epilogue of one run of VEC consecutive outputs along C's contiguous
-// dimension: v = act(alpha*acc + beta*C + bias).  `go` is the line (row of
-// a row-major C, column of a column-major one), `gi` the first element of
-// the run along the line, `lim` the line length; elements past lim are
 // left untouched.  `bias_run` points at the staged bias of the run's first
 // column.  The branches on beta / bias / act are uniform.
 template <int VEC>
@@ -47,7 +42,7 @@ __device__ __forceinline__ void run_epilogue(const GemmArgs &g, int64_t b, int64
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
             if (gi + e < lim)
-                v[e] = fmaf(g.beta, load_as_f32(g.C, g.c_bf16, base + e), v[e]);
+                v[e] = fmaf(g.beta, load_as_f32(g.C, g.c_type, base + e), v[e]);
     }
     if (g.bias) {
 #pragma unroll
@@ -62,20 +57,20 @@ __device__ __forceinline__ void run_epilogue(const GemmArgs &g, int64_t b, int64
 }
 
 // Store rows [r0, r0 + ROWS) of a BM x BN output tile from an LDS chunk
-// (fp32, row-major, row stride LD) to C, or when PARTIAL to the split-K
-// workspace ([split][batch][M][N], row-major).  The NT threads walk C's
-// contiguous dimension in runs of VEC elements (16 bytes: 8 bf16 or 4
-// fp32); a run inside the matrix and 16-byte aligned is written with one
-// vector store, otherwise element by element (ragged edges, odd ldc).
-template <int VEC, bool PARTIAL, bool BF16_OUT, int ROWS, int BN, int LD, int NT>
+// (fp32, row-major, row stride LD) to C of dtype OUT.  The NT threads walk
+// C's contiguous dimension in runs of VEC elements (16 bytes: 8 16-bit or
+// 4 fp32 values); a run inside the matrix and 16-byte aligned is written
+// with one vector store, otherwise element by element (ragged edges, odd
+// ldc).  Serves column-major C (row-major C takes tile_epilogue_rows).
+template <int OUT, int ROWS, int BN, int LD, int NT>
 __device__ __forceinline__ void store_chunk(const GemmArgs &g, const TileCoord &tc,
                                             const float *chunk, int64_t m0, int64_t n0, int r0,
                                             const float *bias_s)
 {
-    const bool col_major = !PARTIAL && g.c_col;
-    const int64_t ld = PARTIAL ? g.N : g.ldc;
-    const int64_t base = PARTIAL ? ((int64_t)tc.s * g.sched.batch + tc.b) * g.M * g.N
-                                 : tc.b * g.sc;
+    constexpr int VEC = OUT == DT_F32 ? 4 : 8;
+    const bool col_major = g.c_col;
+    const int64_t ld = g.ldc;
+    const int64_t base = tc.b * g.sc;
     // runs per line: along n (row-major) or along m (column-major)
     const int line_len = col_major ? ROWS : BN;
     const int runs_per_line = line_len / VEC;
@@ -96,13 +91,11 @@ __device__ __forceinline__ void store_chunk(const GemmArgs &g, const TileCoord &
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
             v[e] = col_major ? chunk[(row - r0 + e) * LD + col] : chunk[(row - r0) * LD + col + e];
-        if (!PARTIAL)
-            run_epilogue<VEC>(g, tc.b, go, gi, inner_lim, col_major, v,
-                              bias_s + col);
+        run_epilogue<VEC>(g, tc.b, go, gi, inner_lim, col_major, v, bias_s + col);
         const int64_t off = base + go * ld + gi;
         const bool full = gi + VEC <= inner_lim;
-        if (PARTIAL || !BF16_OUT) {
-            float *dst = (PARTIAL ? g.ws : (float *)g.C) + off;
+        if (OUT == DT_F32) {
+            float *dst = (float *)g.C + off;
             if (full && ((uintptr_t)dst & 15) == 0) {
                 *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
             } else {
@@ -116,7 +109,7 @@ __device__ __forceinline__ void store_chunk(const GemmArgs &g, const TileCoord &
             uint16_t h[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
-                h[e] = f32_to_bf16(v[e]);
+                h[e] = f32_to_half<OUT>(v[e]);
             if (full && ((uintptr_t)dst & 15) == 0) {
                 uint32_t w[VEC / 2];
 #pragma unroll
@@ -175,8 +168,9 @@ __device__ __forceinline__ void stage_chunk(float *chunk, int c,
 }
 
 // Epilogue of a tile of a row-major output (C, or the split-K workspace
-// when PARTIAL), at any alignment and with ragged edges.  Each output row
-// is cut into 16-byte aligned runs of VEC elements (8 bf16 or 4 fp32) at
+// when PARTIAL, fp32), of dtype OUT, at any alignment and with ragged
+// edges.  Each output row is cut into 16-byte aligned runs of VEC elements
+// (8 16-bit or 4 fp32 values) at
 // its own alignment: a row whose first element sits delta elements past a
 // 16-byte boundary has a partial head run, BN / VEC - 1 full runs and a
 // partial tail.  The row is staged shifted by delta in LDS, so every run
@@ -186,16 +180,18 @@ __device__ __forceinline__ void stage_chunk(float *chunk, int c,
 // `out` points at the tile's first element, `ld` is the output's row
 // stride (elements), rows x cols the part of the tile inside the output and
 // n0 the tile's first column (for the bias).
-template <int BM, int BN, int WM, int WN, bool PARTIAL, bool BF16_OUT>
+template <int BM, int BN, int WM, int WN, bool PARTIAL, int OUT>
 __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out, int64_t ld,
                                                    int rows, int cols, int64_t n0, float *lds,
                                                    const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
 {
     constexpr int NT = 64 * WM * WN;
     constexpr int EP_ROWS = kEpilogueRows, EP_LD = epilogue_ld(BN);
-    constexpr int VEC = BF16_OUT ? 8 : 4;             // outputs per 16-byte run
+    static_assert(!PARTIAL || OUT == DT_F32, "partials are fp32");
+    constexpr bool HALF_OUT = OUT != DT_F32;
+    constexpr int VEC = HALF_OUT ? 8 : 4;             // outputs per 16-byte run
     constexpr int RPR = BN / VEC + 1;                 // runs per row (head + full + tail)
-    constexpr int ES = BF16_OUT ? 2 : 4;              // output element size
+    constexpr int ES = HALF_OUT ? 2 : 4;              // output element size
     static_assert(epilogue_ld(BN) >= BN + VEC - 1, "room for the row shift");
     const int tid = threadIdx.x;
     float *chunk = lds;
@@ -208,7 +204,7 @@ __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out,
     const bool has_bias = !PARTIAL && g.bias;
     if (has_bias) {
         for (int t = tid; t < BN; t += NT)
-            bias_s[t] = t < cols ? load_as_f32(g.bias, g.bias_bf16, n0 + t) : 0.0f;
+            bias_s[t] = t < cols ? load_as_f32(g.bias, g.bias_type, n0 + t) : 0.0f;
     }
 #pragma unroll
     for (int c = 0; c < BM / EP_ROWS; ++c) {
@@ -240,7 +236,7 @@ __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out,
                         const uint32_t w[4] = {cin.x, cin.y, cin.z, cin.w};
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) {
-                            const float x = BF16_OUT ? bf16_to_f32((uint16_t)(w[e / 2] >> (16 * (e % 2))))
+                            const float x = HALF_OUT ? half_to_f32<OUT>((uint16_t)(w[e / 2] >> (16 * (e % 2))))
                                                      : __uint_as_float(w[e]);
                             v[e] = fmaf(g.beta, x, v[e]);
                         }
@@ -248,7 +244,7 @@ __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out,
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) {
                             if (e >= lo && e < hi) {
-                                const float x = BF16_OUT ? bf16_to_f32(((const uint16_t *)dst)[e])
+                                const float x = HALF_OUT ? half_to_f32<OUT>(((const uint16_t *)dst)[e])
                                                          : ((const float *)dst)[e];
                                 v[e] = fmaf(g.beta, x, v[e]);
                             }
@@ -268,11 +264,11 @@ __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out,
                         v[e] = activate(v[e], g.act);
                 }
             }
-            if (BF16_OUT) {
+            if (HALF_OUT) {
                 uint16_t h[VEC];
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
-                    h[e] = f32_to_bf16(v[e]);
+                    h[e] = f32_to_half<OUT>(v[e]);
                 if (full) {
                     uint32_t w[4];
 #pragma unroll
@@ -303,7 +299,7 @@ __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out,
 // Stage and store the whole tile.  `lds` must hold epilogue_lds_bytes(BN)
 // bytes and no wave may still be reading it for other purposes.  Row-major
 // outputs (and split-K partials) take tile_epilogue_rows; a column-major C
-// goes through the masked, element-wise store_chunk.
+// goes through store_chunk.
 template <int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs &g, const TileCoord &tc, float *lds,
                                               int64_t m0, int64_t n0,
@@ -313,19 +309,23 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs &g, const TileCoord
     const int cols = (int)(g.N - n0 < BN ? g.N - n0 : BN);
     if (g.write_partial) {
         float *out = g.ws + (((int64_t)tc.s * g.sched.batch + tc.b) * g.M + m0) * g.N + n0;
-        tile_epilogue_rows<BM, BN, WM, WN, true, false>(g, (char *)out, g.N, rows, cols, n0, lds,
-                                                        acc);
+        tile_epilogue_rows<BM, BN, WM, WN, true, DT_F32>(g, (char *)out, g.N, rows, cols, n0,
+                                                         lds, acc);
         return;
     }
     if (!g.c_col) {
-        if (g.c_bf16) {
-            char *out = (char *)g.C + (tc.b * g.sc + m0 * g.ldc + n0) * 2;
-            tile_epilogue_rows<BM, BN, WM, WN, false, true>(g, out, g.ldc, rows, cols, n0, lds,
-                                                            acc);
-        } else {
+        if (g.c_type == DT_F32) {
             char *out = (char *)g.C + (tc.b * g.sc + m0 * g.ldc + n0) * 4;
-            tile_epilogue_rows<BM, BN, WM, WN, false, false>(g, out, g.ldc, rows, cols, n0, lds,
-                                                             acc);
+            tile_epilogue_rows<BM, BN, WM, WN, false, DT_F32>(g, out, g.ldc, rows, cols, n0, lds,
+                                                              acc);
+        } else {
+            char *out = (char *)g.C + (tc.b * g.sc + m0 * g.ldc + n0) * 2;
+            if (g.c_type == DT_BF16)
+                tile_epilogue_rows<BM, BN, WM, WN, false, DT_BF16>(g, out, g.ldc, rows, cols, n0,
+                                                                   lds, acc);
+            else
+                tile_epilogue_rows<BM, BN, WM, WN, false, DT_F16>(g, out, g.ldc, rows, cols, n0,
+                                                                  lds, acc);
         }
         return;
     }
@@ -336,23 +336,20 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs &g, const TileCoord
     float *chunk = lds;
     // the tile's BN bias values, read from global memory once
     float *bias_s = chunk + EP_ROWS * EP_LD;
-    if (g.bias && !g.write_partial) {
+    if (g.bias) {
         for (int t = tid; t < BN; t += NT)
-            bias_s[t] = n0 + t < g.N ? load_as_f32(g.bias, g.bias_bf16, n0 + t) : 0.0f;
+            bias_s[t] = n0 + t < g.N ? load_as_f32(g.bias, g.bias_type, n0 + t) : 0.0f;
     }
 #pragma unroll
     for (int c = 0; c < BM / EP_ROWS; ++c) {
         stage_chunk<BM, BN, WM, WN>(chunk, c, acc, [](int) { return 0; });
         lds_barrier();
-        if (g.write_partial)
-            store_chunk<4, true, false, EP_ROWS, BN, EP_LD, NT>(g, tc, chunk, m0, n0, c * EP_ROWS,
-                                                                  bias_s);
-        else if (g.c_bf16)
-            store_chunk<8, false, true, EP_ROWS, BN, EP_LD, NT>(g, tc, chunk, m0, n0, c * EP_ROWS,
-                                                                  bias_s);
+        if (g.c_type == DT_BF16)
+            store_chunk<DT_BF16, EP_ROWS, BN, EP_LD, NT>(g, tc, chunk, m0, n0, c * EP_ROWS, bias_s);
+        else if (g.c_type == DT_F16)
+            store_chunk<DT_F16, EP_ROWS, BN, EP_LD, NT>(g, tc, chunk, m0, n0, c * EP_ROWS, bias_s);
         else
-            store_chunk<4, false, false, EP_ROWS, BN, EP_LD, NT>(g, tc, chunk, m0, n0, c * EP_ROWS,
-                                                                   bias_s);
+            store_chunk<DT_F32, EP_ROWS, BN, EP_LD, NT>(g, tc, chunk, m0, n0, c * EP_ROWS, bias_s);
         lds_barrier();
     }
 }

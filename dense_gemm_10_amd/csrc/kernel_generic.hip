@@ -23,7 +23,7 @@ namespace {
 
 constexpr int GBM = 64, GBN = 64, GBK = 16, GTHREADS = 256;
 
-template <bool A_BF16, bool B_BF16>
+template <int AB_TYPE>
 __global__ __launch_bounds__(GTHREADS) void gemm_generic_kernel(GemmArgs g)
 {
     __shared__ float As[GBK][GBM + 1];
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_generic_kernel(GemmArgs g)
                 const int64_t gm = m0 + mm, gk = k0 + kk;
                 float v = 0.0f;
                 if (gm < g.M && gk < ke)
-                    v = load_as_f32(g.A, A_BF16, abase + elem_offset(g.a_col, g.lda, gm, gk));
+                    v = load_as_f32(g.A, AB_TYPE, abase + elem_offset(g.a_col, g.lda, gm, gk));
                 As[kk][mm] = v;
             }
             // B tile: 16 k x 64 columns.
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_generic_kernel(GemmArgs g)
                 const int64_t gn = n0 + nn, gk = k0 + kk;
                 float v = 0.0f;
                 if (gn < g.N && gk < ke)
-                    v = load_as_f32(g.B, B_BF16, bbase + elem_offset(g.b_col, g.ldb, gk, gn));
+                    v = load_as_f32(g.B, AB_TYPE, bbase + elem_offset(g.b_col, g.ldb, gk, gn));
                 Bs[kk][nn] = v;
             }
             __syncthreads();
@@ -173,10 +173,12 @@ hipError_t launch_generic(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
     dim3 grid((unsigned)p.programs), block(GTHREADS);
     // A and B share a dtype (validated on the host).
-    if (g.ab_bf16)
-        hipLaunchKernelGGL((gemm_generic_kernel<true, true>), grid, block, 0, stream, g);
+    if (g.ab_type == DT_BF16)
+        hipLaunchKernelGGL((gemm_generic_kernel<DT_BF16>), grid, block, 0, stream, g);
+    else if (g.ab_type == DT_F16)
+        hipLaunchKernelGGL((gemm_generic_kernel<DT_F16>), grid, block, 0, stream, g);
     else
-        hipLaunchKernelGGL((gemm_generic_kernel<false, false>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((gemm_generic_kernel<DT_F32>), grid, block, 0, stream, g);
     return hipGetLastError();
 }
 

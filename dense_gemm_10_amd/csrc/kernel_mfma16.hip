@@ -1,5 +1,7 @@
-// bf16 GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16), fp32
-// accumulation.
+// bf16 and fp16 GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16 and
+// its fp16 twin v_mfma_f32_32x32x16_f16), fp32 accumulation.  The two
+// element types share every byte of the data path (loads, LDS layout,
+// fragments, epilogue); only the MFMA instruction differs.
 //
 // The structure is the tiled blocked GEMM of "GEMM Kernel Optimization"
 // (Core Technique: one workgroup per BM x BN output tile, K walked in
@@ -24,7 +26,7 @@
 //     half lines were measured to cap the L2 -> CU stream at about 80 % of
 //     what whole lines reach.
 //   LDS layout: a stage row (one row of A, or one column of B) is BK * 2
-//     bytes = CPR chunks of 8 bf16; logical chunk c of row r is stored at
+//     bytes = CPR chunks of 8 16-bit elements; logical chunk c of row r is stored at
 //     slot c ^ ((r / (16 / CPR)) mod CPR).  The LDS serves a 128-bit access
 //     16 lanes at a time over 256 bytes of banks; 16 lanes reading one
 //     logical chunk of 16 consecutive rows then hit 16 different 16-byte
@@ -45,8 +47,8 @@
 // M (or N) are clamped to the last row: the loads stay inside the matrix
 // and those rows only feed outputs that are never stored.
 //
-// Requirements checked on the host: bf16 A (row-major) and B (column-
-// major); 16-byte aligned base pointers; lda, ldb and the batch strides
+// Requirements checked on the host: bf16 or fp16 A (row-major) and B
+// (column-major), of one type; 16-byte aligned base pointers; lda, ldb and the batch strides
 // multiples of 8 elements; BM * lda and BN * ldb small enough for 32-bit
 // byte offsets inside a tile.
 #include "epilogue.hpp"
@@ -57,6 +59,21 @@ namespace dg {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// Fragment type of element type T, and the 32 x 32 x 16 MFMA on it.
+template <int T> struct frag_of { using type = bf16x8_t; };
+template <> struct frag_of<DT_F16> { using type = f16x8_t; };
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(f16x8_t a, f16x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 
 // s_waitcnt immediate: wait until at most n vector-memory loads of this
@@ -91,7 +108,7 @@ __device__ __forceinline__ void dma_16(const void *base, uint32_t voff, uint32_t
                  : "memory", "m0");
 }
 
-// 8 bf16 of one row at k = k_first .. k_first+7, zero for k >= ke (the
+// 8 16-bit elements of one row at k = k_first .. k_first+7, zero for k >= ke (the
 // K-boundary mask of a partial K tile).  `row` points at k = 0 of the row;
 // ke >= 1.  A chunk wholly inside the range is one 16-byte load (the row's
 // chunks are 16-byte aligned: lda is a multiple of 8 and the base
@@ -127,10 +144,11 @@ __device__ __forceinline__ int swizzle_key(int r)
 // One output tile (or, for stream-K, one K range of it): K loop over
 // [kb, ke) and the epilogue, or the raw fp32 accumulators written to `part`
 // (a BM x BN row-major slot) when `part` is not null.
-template <int BM, int BN, int WM, int WN, int kStages, int MBK>
-__device__ __forceinline__ void mfma_bf16_tile(const GemmArgs &g, TileCoord tc, int64_t kb,
-                                               int64_t ke, float *part, uint4 *lds)
+template <int T, int BM, int BN, int WM, int WN, int kStages, int MBK>
+__device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int64_t kb,
+                                            int64_t ke, float *part, uint4 *lds)
 {
+    using frag_t = typename frag_of<T>::type;
     constexpr int NT = 64 * WM * WN;
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;    // wave tile
@@ -241,30 +259,30 @@ __device__ __forceinline__ void mfma_bf16_tile(const GemmArgs &g, TileCoord tc, 
     const int swz = swizzle_key<CPR>(frag_row);   // key of every fragment row (period 16)
 
     // Fragments of k-step ks (0 .. KS-1) of a stage.
-    auto load_frags = [&](int st, int ks, bf16x8_t *af, bf16x8_t *bf) {
+    auto load_frags = [&](int st, int ks, frag_t *af, frag_t *bf) {
         const uint4 *as = lds + st * STAGE_SLOTS + (wm * TM + frag_row) * CPR;
         const uint4 *bs = lds + st * STAGE_SLOTS + (BM + wn * TN + frag_row) * CPR;
         const int c = (ks * 2 + frag_half) ^ swz;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            af[i] = __builtin_bit_cast(bf16x8_t, as[i * 32 * CPR + c]);
+            af[i] = __builtin_bit_cast(frag_t, as[i * 32 * CPR + c]);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            bf[j] = __builtin_bit_cast(bf16x8_t, bs[j * 32 * CPR + c]);
+            bf[j] = __builtin_bit_cast(frag_t, bs[j * 32 * CPR + c]);
     };
 
-    auto mfma_step = [&](const bf16x8_t *af, const bf16x8_t *bf) {
+    auto mfma_step = [&](const frag_t *af, const frag_t *bf) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = mfma_32x32x16(af[i], bf[j], acc[i][j]);
     };
 
     // Two fragment register sets, alternating per k-step; fa[1]/fb[1]
     // carry the last k-step of a stage into the next iteration, whose MFMAs
     // run after the barrier while the new stage's first fragments are read.
-    bf16x8_t fa[2][FM], fb[2][FN];
+    frag_t fa[2][FM], fb[2][FN];
 
     // One stage, as KS k-steps of FM * FN fenced slots.  Slot n of k-step ks
     // issues the MFMA of block n on the previous k-step's fragments and,
@@ -293,12 +311,11 @@ __device__ __forceinline__ void mfma_bf16_tile(const GemmArgs &g, TileCoord tc, 
 #pragma unroll
             for (int n = 0; n < FM * FN; ++n) {
                 if (n < FM)
-                    fa[cur][n] = __builtin_bit_cast(bf16x8_t, as[n * 32 * CPR + c]);
+                    fa[cur][n] = __builtin_bit_cast(frag_t, as[n * 32 * CPR + c]);
                 else if (n < FM + FN)
-                    fb[cur][n - FM] = __builtin_bit_cast(bf16x8_t, bs[(n - FM) * 32 * CPR + c]);
+                    fb[cur][n - FM] = __builtin_bit_cast(frag_t, bs[(n - FM) * 32 * CPR + c]);
                 const int i = n / FN, j = n % FN;
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[prev][i], fb[prev][j],
-                                                                    acc[i][j], 0, 0, 0);
+                acc[i][j] = mfma_32x32x16(fa[prev][i], fb[prev][j], acc[i][j]);
                 const int d = ks * FM * FN + n;
                 if (dma && (d % MFMA_PER_DMA) == MFMA_PER_DMA - 1 && d / MFMA_PER_DMA < LPW)
                     issue_dma_one(v_dma, d / MFMA_PER_DMA);
@@ -320,10 +337,10 @@ __device__ __forceinline__ void mfma_bf16_tile(const GemmArgs &g, TileCoord tc, 
     if (g.alpha != 0.0f && ntiles > 0) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            fa[1][i] = bf16x8_t{};
+            fa[1][i] = frag_t{};
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            fb[1][j] = bf16x8_t{};
+            fb[1][j] = frag_t{};
         // prologue: tiles 0 .. D-1
         for (int64_t v = 0; v < D && v < ntiles; ++v) {
             if (v == 0 && tail)
@@ -354,8 +371,8 @@ __device__ __forceinline__ void mfma_bf16_tile(const GemmArgs &g, TileCoord tc, 
     static_assert(epilogue_lds_bytes(BN) <= kStages * STAGE_SLOTS * 16,
                   "epilogue chunk and bias fit in LDS");
     if (part)
-        tile_epilogue_rows<BM, BN, WM, WN, true, false>(g, (char *)part, BN, BM, BN, n0,
-                                                        (float *)lds, acc);
+        tile_epilogue_rows<BM, BN, WM, WN, true, DT_F32>(g, (char *)part, BN, BM, BN, n0,
+                                                         (float *)lds, acc);
     else
         tile_epilogue<BM, BN, WM, WN>(g, tc, (float *)lds, m0, n0, acc);
 }
@@ -364,10 +381,9 @@ __device__ __forceinline__ void mfma_bf16_tile(const GemmArgs &g, TileCoord tc, 
 // Stream-K launches give programs [0, dp_tiles) one whole tile each and the
 // others one K slice of a tail tile, written as a raw fp32 partial that the
 // fix-up kernel adds up.
-template <int BM, int BN, int WM, int WN, int kStages, int MBK>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g)
+template <int T, int BM, int BN, int WM, int WN, int kStages, int MBK>
+__device__ __forceinline__ void mfma16_program(const GemmArgs &g, uint4 *lds)
 {
-    extern __shared__ uint4 lds[];
     const StreamK &sk = g.sk;
     const int64_t pid = blockIdx.x;
     TileCoord tc;
@@ -391,16 +407,35 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g
         ke = kb + sk.k_per_split < g.K ? kb + sk.k_per_split : g.K;
         part = g.sk_parts + (r * sk.tail_splits + slice) * (int64_t)(BM * BN);
     }
-    mfma_bf16_tile<BM, BN, WM, WN, kStages, MBK>(g, tc, kb, ke, part, lds);
+    mfma16_tile<T, BM, BN, WM, WN, kStages, MBK>(g, tc, kb, ke, part, lds);
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int BK>
+// One kernel name per element type, so that traces tell them apart.
+template <int BM, int BN, int WM, int WN, int kStages, int MBK>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g)
+{
+    extern __shared__ uint4 lds[];
+    mfma16_program<DT_BF16, BM, BN, WM, WN, kStages, MBK>(g, lds);
+}
+
+template <int BM, int BN, int WM, int WN, int kStages, int MBK>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f16_kernel(GemmArgs g)
+{
+    extern __shared__ uint4 lds[];
+    mfma16_program<DT_F16, BM, BN, WM, WN, kStages, MBK>(g, lds);
+}
+
+template <int T, int BM, int BN, int WM, int WN, int NS, int BK>
 hipError_t launch_one(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
     const size_t lds_bytes = (size_t)NS * (BM + BN) * (BK / 8) * sizeof(uint4);
-    auto kern = gemm_mfma_bf16_kernel<BM, BN, WM, WN, NS, BK>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)p.programs), dim3(64 * WM * WN), lds_bytes, stream,
-                       g);
+    const dim3 grid((unsigned)p.programs), block(64 * WM * WN);
+    if constexpr (T == DT_F16)
+        hipLaunchKernelGGL((gemm_mfma_f16_kernel<BM, BN, WM, WN, NS, BK>), grid, block, lds_bytes,
+                           stream, g);
+    else
+        hipLaunchKernelGGL((gemm_mfma_bf16_kernel<BM, BN, WM, WN, NS, BK>), grid, block, lds_bytes,
+                           stream, g);
     return hipGetLastError();
 }
 
@@ -410,7 +445,8 @@ hipError_t launch_one(const GemmArgs &g, const Plan &p, hipStream_t stream)
 // Entries 0 and 1 are the large and small tiles of the automatic choice:
 // 256 x 256 with whole-line (BK = 64) stages in a 2-stage ring, and
 // 128 x 128 with BK = 32 in a 4-stage ring (64 KB of LDS, two workgroups
-// per CU).  The others are selectable by name for sweeps.
+// per CU).  The others are selectable by name for sweeps.  The fp16 table
+// holds the two tiles of the automatic choice.
 const TileConfig kMfmaBf16Tiles[] = {
     {256, 256, 64, 256, 5, "mfma_bf16_256x256x64_w2x2_s2", 1},
     {128, 128, 32, 256, 1, "mfma_bf16_128x128x32_w2x2_s4", 2},
@@ -423,17 +459,30 @@ const TileConfig kMfmaBf16Tiles[] = {
 };
 const int kNumMfmaBf16Tiles = 8;
 
-hipError_t launch_mfma_bf16(const GemmArgs &g, const Plan &p, hipStream_t stream)
+const TileConfig kMfmaF16Tiles[] = {
+    {256, 256, 64, 256, 5, "mfma_f16_256x256x64_w2x2_s2", 1},
+    {128, 128, 32, 256, 1, "mfma_f16_128x128x32_w2x2_s4", 2},
+};
+const int kNumMfmaF16Tiles = 2;
+
+hipError_t launch_mfma16(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
+    if (g.ab_type == DT_F16) {
+        switch (p.tile.variant) {
+        case 1: return launch_one<DT_F16, 128, 128, 2, 2, 4, 32>(g, p, stream);
+        case 5: return launch_one<DT_F16, 256, 256, 2, 2, 2, 64>(g, p, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (p.tile.variant) {
-    case 0: return launch_one<256, 256, 2, 2, 4, 32>(g, p, stream);
-    case 1: return launch_one<128, 128, 2, 2, 4, 32>(g, p, stream);
-    case 2: return launch_one<256, 128, 2, 2, 4, 32>(g, p, stream);
-    case 3: return launch_one<256, 128, 2, 2, 3, 32>(g, p, stream);
-    case 4: return launch_one<128, 256, 2, 2, 3, 32>(g, p, stream);
-    case 5: return launch_one<256, 256, 2, 2, 2, 64>(g, p, stream);
-    case 6: return launch_one<128, 128, 2, 2, 3, 64>(g, p, stream);
-    case 7: return launch_one<256, 128, 2, 2, 3, 64>(g, p, stream);
+    case 0: return launch_one<DT_BF16, 256, 256, 2, 2, 4, 32>(g, p, stream);
+    case 1: return launch_one<DT_BF16, 128, 128, 2, 2, 4, 32>(g, p, stream);
+    case 2: return launch_one<DT_BF16, 256, 128, 2, 2, 4, 32>(g, p, stream);
+    case 3: return launch_one<DT_BF16, 256, 128, 2, 2, 3, 32>(g, p, stream);
+    case 4: return launch_one<DT_BF16, 128, 256, 2, 2, 3, 32>(g, p, stream);
+    case 5: return launch_one<DT_BF16, 256, 256, 2, 2, 2, 64>(g, p, stream);
+    case 6: return launch_one<DT_BF16, 128, 128, 2, 2, 3, 64>(g, p, stream);
+    case 7: return launch_one<DT_BF16, 256, 128, 2, 2, 3, 64>(g, p, stream);
     default: return hipErrorInvalidValue;
     }
 }

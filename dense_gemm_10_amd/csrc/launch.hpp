@@ -12,6 +12,7 @@ enum Kernel {
     KERNEL_VALU_F32 = 2,
     KERNEL_MFMA_BF16 = 3,
     KERNEL_MFMA_F32 = 4,
+    KERNEL_MFMA_F16 = 5,
 };
 
 // One tile configuration of a kernel family.
@@ -39,7 +40,8 @@ struct Plan {
 // launch error.
 hipError_t launch_generic(const GemmArgs &g, const Plan &p, hipStream_t stream);
 hipError_t launch_valu_f32(const GemmArgs &g, const Plan &p, hipStream_t stream);
-hipError_t launch_mfma_bf16(const GemmArgs &g, const Plan &p, hipStream_t stream);
+// bf16 and fp16 matrix-core kernels (element type from g.ab_type)
+hipError_t launch_mfma16(const GemmArgs &g, const Plan &p, hipStream_t stream);
 hipError_t launch_mfma_f32(const GemmArgs &g, const Plan &p, hipStream_t stream);
 hipError_t launch_splitk_reduce(const GemmArgs &g, const Plan &p, hipStream_t stream);
 hipError_t launch_streamk_fixup(const GemmArgs &g, const Plan &p, hipStream_t stream);
@@ -49,6 +51,8 @@ extern const TileConfig kGenericTiles[];
 extern const TileConfig kValuTiles[];
 extern const TileConfig kMfmaBf16Tiles[];
 extern const TileConfig kMfmaF32Tiles[];
-extern const int kNumGenericTiles, kNumValuTiles, kNumMfmaBf16Tiles, kNumMfmaF32Tiles;
+extern const TileConfig kMfmaF16Tiles[];
+extern const int kNumGenericTiles, kNumValuTiles, kNumMfmaBf16Tiles, kNumMfmaF32Tiles,
+    kNumMfmaF16Tiles;
 
 } // namespace dg

@@ -56,8 +56,13 @@ typedef enum {
     DG_ERROR_LAUNCH = 4                  /* the runtime refused a kernel launch */
 } dg_status;
 
-/* Element types.  DG_BF16 is bfloat16: the top 16 bits of an IEEE fp32. */
-typedef enum { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
+/* Element types.  DG_BF16 is bfloat16: the top 16 bits of an IEEE fp32.
+ * DG_F16 is IEEE 754 binary16 (5 exponent bits, 10 fraction bits; largest
+ * finite value 65504).  Inputs in fp16 are the dtype of the pages' own
+ * correctness check ("Skill: Write a Triton GEMM Kernel", Inputs the agent
+ * should gather first, and the allclose check of "GEMM Kernel
+ * Optimization", Verification). */
+typedef enum { DG_F32 = 0, DG_BF16 = 1, DG_F16 = 2 } dg_dtype;
 
 /* Storage order of one operand.  Row-major X (R x C) with leading dimension
  * ld holds X[r][c] at element r*ld + c; column-major holds it at c*ld + r. */
@@ -74,14 +79,18 @@ typedef enum { DG_ACT_NONE = 0, DG_ACT_GELU_ERF = 1, DG_ACT_GELU_TANH = 2 } dg_a
  * matrix-core kernel (MFMA_F32) when the operands are 16-byte aligned with
  * leading dimensions and batch strides multiple of 4; VALU_F32 (the
  * register-tiled vector-FMA kernel) takes the same operands and is used
- * only when asked for.  Forcing a family whose requirements the operands
- * do not meet returns DG_ERROR_NOT_SUPPORTED. */
+ * only when asked for.  bf16 and fp16 inputs go to their matrix-core kernel
+ * (MFMA_BF16, MFMA_F16) when A is row-major and B column-major, both
+ * 16-byte aligned with leading dimensions and batch strides multiple of 8.
+ * Forcing a family whose requirements the operands do not meet returns
+ * DG_ERROR_NOT_SUPPORTED. */
 typedef enum {
     DG_ALGO_AUTO = 0,
     DG_ALGO_GENERIC = 1,
     DG_ALGO_VALU_F32 = 2,  /* register-tiled fp32 outer-product kernel */
     DG_ALGO_MFMA_BF16 = 3, /* bf16 matrix-core kernel */
-    DG_ALGO_MFMA_F32 = 4   /* fp32 matrix-core kernel */
+    DG_ALGO_MFMA_F32 = 4,  /* fp32 matrix-core kernel */
+    DG_ALGO_MFMA_F16 = 5   /* fp16 matrix-core kernel (the bf16 kernel's twin) */
 } dg_algo;
 
 /* Work distribution over the compute units (benchmarking and ablation; 0
@@ -92,10 +101,10 @@ typedef enum {
  * data-parallel, and the K range of each remaining (tail) tile is cut into
  * slices, one workgroup each, enough to fill one more wave; a second, small
  * kernel adds each tail tile's fp32 partials in slice order (fixed order, no
- * atomics) and applies the epilogue.  STREAM_K applies to the bf16
- * matrix-core kernel with batch == 1 and split_k <= 1 and needs workspace
+ * atomics) and applies the epilogue.  STREAM_K applies to the bf16 and fp16
+ * matrix-core kernels with batch == 1 and split_k <= 1 and needs workspace
  * (see dg_gemm_workspace_size); otherwise DG_ERROR_NOT_SUPPORTED.  The
- * automatic choice uses it only for that kernel, when the last wave of
+ * automatic choice uses it only for those kernels, when the last wave of
  * tiles would be less than 85 % full, K >= 2048 and the caller passes
  * enough workspace. */
 typedef enum {
@@ -112,8 +121,11 @@ typedef enum {
  *                   gives C = act(beta*C + bias).
  *   batch           >= 0; 0 is a no-op.
  *   a_type, b_type  input types; c_type output type.  Supported
- *                   (a, b, c): (F32, F32, F32), (BF16, BF16, BF16),
- *                   (BF16, BF16, F32).  Accumulation is always fp32.
+ *                   (a, b, c): (F32, F32, F32), and for 16-bit inputs
+ *                   (X, X, c) with X = BF16 or F16 and c = F32, BF16 or
+ *                   F16.  Accumulation is always fp32; a 16-bit output is
+ *                   rounded to nearest, ties to even (fp16 beyond 65504
+ *                   rounds to infinity).
  *   a_order ...     storage order of A (M x K), B (K x N), C (M x N).
  *   lda, ldb, ldc   leading dimensions, each >= max(1, length of the
  *                   contiguous dimension) (e.g. row-major A: lda >= K).
@@ -122,7 +134,7 @@ typedef enum {
  *                   stride_c must not make two C matrices overlap.
  *   alpha, beta     host scalars.  beta == 0: C is not read (NaN in C does
  *                   not propagate).  alpha == 0: A and B are not read.
- *   bias, bias_type optional DEVICE vector of N elements (F32 or BF16),
+ *   bias, bias_type optional DEVICE vector of N elements (F32, BF16 or F16),
  *                   added to every row; NULL for none.
  *   act             activation, see dg_act.
  *   split_k         0: the library decides (it only splits K when the

@@ -121,6 +121,8 @@ def test_bad_struct_size():
 @pytest.mark.parametrize("kw", [dict(a_type="f32", b_type="bf16"),
                                 dict(a_type="bf16", b_type="f32"),
                                 dict(a_type="f32", c_type="bf16"),
+                                dict(a_type="f16", b_type="bf16"),
+                                dict(a_type="f32", c_type="f16"),
                                 dict(split_k=100000)])
 def test_unsupported_combinations(kw):
     assert _gemm_status(_desc(**kw)) == dg.DG_ERROR_NOT_SUPPORTED
@@ -185,6 +187,33 @@ def test_plans_of_the_five_workloads():
     assert "kernel=mfma_bf16" in c5 and "splits=1 " not in c5
     # without workspace the automatic choice does not split
     assert "splits=1 " in dg.dg_gemm_describe(d5, 0)
+
+
+def test_f16_plans():
+    f = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["f16_4096"]))
+    assert "kernel=mfma_f16" in f and "tile=mfma_f16_256x256x64_w2x2_s2" in f
+    g = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["f16_gelu"]))
+    assert "kernel=mfma_f16" in g and "tile=mfma_f16_128x128x32_w2x2_s4" in g
+    # every output type is accepted for 16-bit inputs
+    for a in ("bf16", "f16"):
+        for c in ("f32", "bf16", "f16"):
+            d = _desc(a_type=a, b_type=a, c_type=c, b_order="col", bias=PW, bias_type="f16")
+            assert f"kernel=mfma_{a}" in dg.dg_gemm_describe(d)
+    # each 16-bit family takes only its own element type
+    for a, algo in (("f16", dg.DG_ALGO_MFMA_BF16), ("bf16", dg.DG_ALGO_MFMA_F16),
+                    ("f32", dg.DG_ALGO_MFMA_F16)):
+        with pytest.raises(dg.DgError) as e:
+            dg.dg_gemm_describe(_desc(a_type=a, b_type=a, b_order="col", algo=algo))
+        assert e.value.status == dg.DG_ERROR_NOT_SUPPORTED
+    # fp16 outside the matrix-core layout goes to the generic kernel
+    assert "kernel=generic" in dg.dg_gemm_describe(_desc(a_type="f16", b_type="f16"))
+    # fp16 pointers need 2-byte alignment
+    assert _gemm_status(_desc(a_type="f16", b_type="f16", c_type="f16"), C=PC + 1) == \
+        dg.DG_ERROR_INVALID_VALUE
+    # forced stream-K on the fp16 kernel
+    sk = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["f16_gelu"].replace(K=4096)),
+                             1 << 34)
+    assert "kernel=mfma_f16" in sk and "schedule=stream_k" in sk and "bm=256" in sk
 
 
 def test_layouts_outside_the_fast_paths_use_the_generic_kernel():

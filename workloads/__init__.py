@@ -201,6 +201,22 @@ WORKLOADS = {
         a_type=F32, b_type=F32, c_type=F32,
         alpha=1.0, beta=0.0,
         dist_a=("uniform", -1.0, 1.0), dist_b=("uniform", -1.0, 1.0), seed=7),
+    # fp16 twins of the 4096^3 GEMM and of the ragged GELU GEMM (fp16 is the
+    # dtype of the allclose check in "GEMM Kernel Optimization",
+    # Verification): same layouts, distributions and sizes.
+    "f16_4096": Problem(
+        name="gemm_f16_4096", M=4096, N=4096, K=4096,
+        a_type=F16, b_type=F16, c_type=F16,
+        a_order=ROW, b_order=COL, c_order=ROW,
+        alpha=1.0, beta=0.0,
+        dist_a=("normal", 1.0), dist_b=("normal", 1.0), seed=9),
+    "f16_gelu": Problem(
+        name="gemm_f16_4095x4097x1000_bias_gelu", M=4095, N=4097, K=1000,
+        a_type=F16, b_type=F16, c_type=F16,
+        a_order=ROW, b_order=COL, c_order=ROW,
+        alpha=1.0, beta=0.0, has_bias=True, bias_type=F16, act=ACT_GELU_ERF,
+        dist_a=("normal", 0.5), dist_b=("normal", 0.5),
+        dist_bias=("uniform", -0.5, 0.5), seed=10),
     "tail4352": Problem(
         name="gemm_bf16_4352x4352x8192", M=4352, N=4352, K=8192,
         a_type=BF16, b_type=BF16, c_type=BF16,
