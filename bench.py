@@ -168,13 +168,16 @@ def _shown(cmd, tmp):
     return text.replace(tmp, "$OUT")
 
 
-def collect_profile(workload, tmp, out_dir=PROFILES):
-    """Kernel-trace statistics and HBM traffic counters of one workload,
-    written to profiles/.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
-    are each scaled by the ratio between the bytes a plain device copy of
-    known size moves and what the same counter reports for it."""
+def collect_profile(workload, tmp, out_dir=PROFILES, knobs=()):
+    """Kernel-trace statistics, HBM traffic and L2 hit counters of one
+    workload, written to profiles/.  FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) are each scaled by the ratio between the bytes a plain device
+    copy of known size moves and what the same counter reports for it.  The
+    L2 hit rate is TCC_HIT / (TCC_HIT + TCC_MISS) over the GEMM dispatches.
+    `knobs` are extra bench.py arguments for the profiled runs (tile order,
+    kernel family)."""
     import subprocess
-    child = ["--workload", workload, "--secondary", "none", "--no-cpu-baseline"]
+    child = ["--workload", workload, "--secondary", "none", "--no-cpu-baseline"] + list(knobs)
     results = {}
     # 1. kernel trace with statistics
     out = os.path.join(tmp, "trace")
@@ -202,8 +205,22 @@ def collect_profile(workload, tmp, out_dir=PROFILES):
                             "copy_kib_per_dispatch": copy_kib, "copy_bytes": 512 << 20,
                             "scale": scale, "bytes_per_dispatch": kib * 1024.0 * scale,
                             "command": _shown(cmd, tmp), "copy_command": _shown(cmd_c, tmp)}
+    # 3. L2 (TCC) hits and misses of the GEMM kernels
+    out = os.path.join(tmp, "tcc")
+    cmd = _rocprof(["--pmc", "TCC_HIT_sum", "TCC_MISS_sum"], out) + child + ["--steps", "3",
+                                                                           "--warmup", "1"]
+    log(f"[profile] {' '.join(cmd)}")
+    subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL)
+    rows = _csv_rows(out, "counter_collection.csv")
+    hit, _ = _per_dispatch([r for r in rows if r["Counter_Name"] == "TCC_HIT_sum"], "gemm_")
+    miss, _ = _per_dispatch([r for r in rows if r["Counter_Name"] == "TCC_MISS_sum"], "gemm_")
+    results["L2"] = {"hits_per_dispatch": hit, "misses_per_dispatch": miss,
+                     "hit_rate": hit / (hit + miss) if hit + miss > 0 else None,
+                     "command": _shown(cmd, tmp)}
     results["kernel_source_hash"] = kernel_source_hash()
     results["workload"] = workload
+    results["knobs"] = list(knobs)
+    results["library"] = os.environ.get("DG_LIBRARY") or "in-tree"
     write_profile(results, out_dir)
     return results
 
@@ -216,10 +233,13 @@ def write_profile(results, out_dir=PROFILES):
         json.dump(results, f, indent=1)
     import workloads as W
     p = W.WORKLOADS[workload]
+    knobs = " ".join(results.get("knobs", []))
+    lib = results.get("library", "in-tree")
     lines = [f"# rocprofv3 summary: {p.name}", "",
-             f"Made by `python3 bench.py --workload {workload} --collect-profile` from the "
-             "repository root, which runs the commands below ($OUT is a temporary folder).", "",
-             f"Kernel sources hash: `{results['kernel_source_hash']}`", "",
+             f"Made by `python3 bench.py --workload {workload} --collect-profile"
+             f"{' ' + knobs if knobs else ''}` from the repository root, which runs the commands "
+             "below ($OUT is a temporary folder).", "",
+             f"Kernel sources hash: `{results['kernel_source_hash']}`; library: {lib}", "",
              "## Kernel trace statistics", "", f"Command: `{results['trace_command']}`", "",
              "| kernel | calls | average ns | min ns | max ns | % |", "|---|---|---|---|---|---|"]
     for r in results["kernel_stats"]:
@@ -236,6 +256,12 @@ def write_profile(results, out_dir=PROFILES):
     lines += ["", f"Commands: `{results['FETCH_SIZE']['command']}`, "
               f"`{results['WRITE_SIZE']['command']}`; calibration: "
               f"`{results['FETCH_SIZE']['copy_command']}`", ""]
+    if "L2" in results:
+        l2 = results["L2"]
+        lines += ["## L2 (TCC) hit rate per GEMM dispatch", "",
+                  "| TCC_HIT | TCC_MISS | hit rate |", "|---|---|---|",
+                  f"| {l2['hits_per_dispatch']:.0f} | {l2['misses_per_dispatch']:.0f} | "
+                  f"{l2['hit_rate']:.3f} |", "", f"Command: `{l2['command']}`", ""]
     with open(os.path.join(out_dir, f"{workload}_{p.name}.md"), "w") as f:
         f.write("\n".join(lines))
 
@@ -250,6 +276,8 @@ def traffic_for(workload):
         t = json.load(f)
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
+    if t.get("knobs") or t.get("library", "in-tree") != "in-tree":
+        return None      # taken with another tile order, family or build
     return t["FETCH_SIZE"]["bytes_per_dispatch"] + t["WRITE_SIZE"]["bytes_per_dispatch"]
 
 
@@ -300,8 +328,13 @@ def main():
 
     if args.collect_profile:
         import tempfile
+        knobs = []
+        for flag, v in (("--algo", args.algo), ("--group-m", args.group_m),
+                        ("--xcd-remap", args.xcd_remap)):
+            if v:
+                knobs += [flag, str(v)]
         with tempfile.TemporaryDirectory(dir=os.environ.get("TMPDIR", "/tmp")) as tmp:
-            r = collect_profile(args.workload, tmp, args.profile_dir)
+            r = collect_profile(args.workload, tmp, args.profile_dir, knobs)
         print(json.dumps({"workload": args.workload,
                           "fetch_bytes": r["FETCH_SIZE"]["bytes_per_dispatch"],
                           "write_bytes": r["WRITE_SIZE"]["bytes_per_dispatch"]}), flush=True)

@@ -26,7 +26,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libdensegemm.so")
+# DG_LIBRARY may name another build of the same sources (a measurement
+# build with compile-time options); by default the in-tree library.
+_LIB_PATH = os.environ.get("DG_LIBRARY") or os.path.join(_HERE, "libdensegemm.so")
 
 # status codes
 DG_SUCCESS = 0

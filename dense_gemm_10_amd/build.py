@@ -5,6 +5,12 @@
 Every HIP source is compiled for gfx950 only, with packed-FP32 instructions
 disabled (-Xclang -target-feature -Xclang -packed-fp32-ops), then linked into
 one shared library next to this file.
+
+Measurement builds with compile-time options go elsewhere:
+
+    python -m dense_gemm_10_amd.build --define DG_LOAD_POLICY_A=nt --out /tmp/lib_nt.so
+
+and are loaded instead of the in-tree library when DG_LIBRARY names them.
 """
 from __future__ import annotations
 
@@ -36,32 +42,44 @@ SOURCES = [
 ]
 
 
-def _compile(src):
+def _compile(src, defines=(), obj_dir=OUT_DIR):
     path = os.path.join(CSRC, src)
-    obj = os.path.join(OUT_DIR, src + ".o")
-    cmd = [HIPCC] + COMMON_FLAGS + ["-x", "hip", "-c", path, "-o", obj]
+    obj = os.path.join(obj_dir, src + ".o")
+    cmd = [HIPCC] + COMMON_FLAGS + [f"-D{d}" for d in defines] + ["-x", "hip", "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose=False):
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(verbose=False, defines=(), out=None):
+    """Compile and link; `defines` (NAME or NAME=VALUE) are passed to every
+    compile, `out` replaces the in-tree library path."""
+    defines = tuple(defines)
+    lib = out or LIB
+    obj_dir = OUT_DIR if not defines else os.path.join(OUT_DIR, "opt_" + "_".join(
+        d.replace("=", "-") for d in defines))
+    os.makedirs(obj_dir, exist_ok=True)
     workers = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + f".tmp{os.getpid()}"
+        objs = list(ex.map(lambda s: _compile(s, defines, obj_dir), SOURCES))
+    tmp = lib + f".tmp{os.getpid()}"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--define", action="append", default=[],
+                    help="NAME or NAME=VALUE passed to every compile (measurement builds)")
+    ap.add_argument("--out", default=None, help="library path (default: in-tree)")
+    a = ap.parse_args()
+    build(verbose=True, defines=a.define, out=a.out)
     sys.exit(0)
