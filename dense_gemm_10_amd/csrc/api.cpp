@@ -217,6 +217,50 @@ const TileConfig *forced_tile(const TileConfig *table, int n)
     return nullptr;
 }
 
+// Offline-tuned plans, generated by dense_gemm_10_amd/tune.py from timed
+// sweeps on an MI355X over every tile configuration of a family and both
+// schedules ("GEMM Kernel Optimization", Autotuning: benchmark the
+// candidate configurations per problem size and keep the fastest; here the
+// sweep runs once, offline, and its winners are compiled in, so no call
+// ever benchmarks).  An exact (family, M, N, K, batch) match replaces the
+// heuristic tile choice and states the schedule and the split-K count; the
+// table ends with an entry whose tile is NULL.  DG_TUNED=0 in the environment switches it off
+// (benchmarking and ablation only).
+struct TunedEntry {
+    int32_t kernel;
+    int64_t M, N, K, batch;
+    const char *tile;
+    int32_t schedule;     // DG_SCHED_DATA_PARALLEL or DG_SCHED_STREAM_K
+    int32_t splits;       // split-K slices; 0: the automatic choice
+};
+
+const TunedEntry kTuned[] = {
+#include "tuned_table.inc"
+    {0, 0, 0, 0, 0, nullptr, 0, 0},
+};
+
+const TileConfig *tile_named(const TileConfig *table, int n, const char *name)
+{
+    for (int i = 0; i < n; ++i)
+        if (strcmp(table[i].name, name) == 0)
+            return &table[i];
+    return nullptr;
+}
+
+// The tuned entry for this problem on kernel family k whose tile exists in
+// `table`, or NULL.
+const TunedEntry *find_tuned(const dg_gemm_desc *d, Kernel k, const TileConfig *table, int n)
+{
+    const char *off = getenv("DG_TUNED");
+    if (off && strcmp(off, "0") == 0)
+        return nullptr;
+    for (const TunedEntry *e = kTuned; e->tile; ++e)
+        if (e->kernel == k && e->M == d->M && e->N == d->N && e->K == d->K &&
+            e->batch == d->batch && tile_named(table, n, e->tile))
+            return e;
+    return nullptr;
+}
+
 // Pick the matrix-core tile.  The 256 x 256 tile (one workgroup per CU) has
 // the best flop-per-byte ratio but quantises badly when its tile count is
 // not close to a whole number of waves over the 256 CUs ("La GEMM, de zero
@@ -244,22 +288,35 @@ TileConfig pick_quantised(const dg_gemm_desc *d, const TileConfig *table, int n)
 
 
 // Split-K slices for `tiles` output tiles: only when the tiles alone leave
-// most compute units idle and every slice keeps a long K range.
+// most compute units idle and every slice keeps a long K range: 1024 for
+// 16-bit inputs, 256 for fp32, whose K steps cost 8 to 16 times more
+// matrix-core time per element (measured at 1024^3 fp32: 42 us in 4 slices
+// against 112 us unsplit).
 int32_t auto_splits(const dg_gemm_desc *d, int64_t tiles)
 {
-    if (!reads_ab(d) || tiles >= kNumCu / 2 || d->K < 2048)
+    const int64_t min_slice = d->a_type == DG_F32 ? 256 : 1024;
+    if (!reads_ab(d) || tiles >= kNumCu / 2 || d->K < 2 * min_slice)
         return 1;
     int64_t s = kNumCu / tiles;                  // about one program per CU
-    int64_t by_k = d->K / 1024;                  // keep >= 1024 of K per slice
+    int64_t by_k = d->K / min_slice;             // keep >= min_slice of K per slice
     if (s > by_k) s = by_k;
     if (s > 16) s = 16;
     return s < 2 ? 1 : (int32_t)s;
 }
 
 // Split-K, stream-K, grid and workspace of a plan whose kernel and tile are
-// chosen.
-dg_status finish_plan(const dg_gemm_desc *d, Plan p, size_t ws_avail, bool ws_known, Plan *plan)
+// chosen.  `tuned_sched` and `tuned_splits` are what a tuned entry states
+// (0 if none): they apply where the caller leaves the choice to the
+// library, and like the automatic choice they never ask for more workspace
+// than given.
+dg_status finish_plan(const dg_gemm_desc *d, Plan p, size_t ws_avail, bool ws_known,
+                      int32_t tuned_sched, int32_t tuned_splits, Plan *plan)
 {
+    const bool forced_sk = d->schedule == DG_SCHED_STREAM_K;
+    const bool lib_sched = d->schedule == DG_SCHED_AUTO;
+    const bool prefer_sk = lib_sched && tuned_sched == DG_SCHED_STREAM_K;
+    const bool forbid_sk = d->schedule == DG_SCHED_DATA_PARALLEL ||
+                           (lib_sched && tuned_sched == DG_SCHED_DATA_PARALLEL);
     const int64_t tiles = tiles_of(d, p.tile);
     const int64_t plane = d->batch * d->M * d->N * (int64_t)sizeof(float);
     int32_t S;
@@ -267,10 +324,10 @@ dg_status finish_plan(const dg_gemm_desc *d, Plan p, size_t ws_avail, bool ws_kn
         S = 1;
     } else if (d->split_k >= 1) {
         S = d->split_k;
-    } else if (d->schedule == DG_SCHED_STREAM_K) {
+    } else if (forced_sk || prefer_sk) {
         S = 1;   // stream-K asked for: no automatic split-K
     } else {
-        S = auto_splits(d, tiles);
+        S = tuned_splits > 0 ? tuned_splits : auto_splits(d, tiles);
         // the automatic choice never asks for more workspace than given
         if (ws_known && S > 1 && (size_t)plane * S > ws_avail)
             S = plane > 0 ? (int32_t)(ws_avail / (size_t)plane) : 1;
@@ -299,16 +356,20 @@ dg_status finish_plan(const dg_gemm_desc *d, Plan p, size_t ws_avail, bool ws_kn
     // full waves stay data-parallel; each of the R tail tiles is cut into S
     // K slices, S about wave / R, so the tail fills one more wave.  Only
     // when the tail wave would be less than 85 % full, every slice keeps at
-    // least two K steps, and, for the automatic choice, K >= 2048 and the
-    // caller gives enough workspace for the R * S fp32 partial tiles.  With
-    // a shorter K the tail tiles' epilogues cost about as much as their K
-    // loop and slicing them gained nothing in measurements (4095 x 4097 x
-    // 1000: 101 vs 103 us with GELU, 91 vs 85 us without).
+    // least two K steps, and, for the automatic choice, there is at least
+    // one full data-parallel wave, K >= 2048 and the caller gives enough
+    // workspace for the R * S fp32 partial tiles.  With a shorter K the tail
+    // tiles' epilogues cost about as much as their K loop and slicing them
+    // gained nothing in measurements (4095 x 4097 x 1000: 101 vs 103 us with
+    // GELU, 91 vs 85 us without).  Without a full wave, the partial-tile
+    // traffic and the fix-up cost more than the idle compute units: 2048^3
+    // ran 41 us sliced against 25 us data-parallel on 128 x 128 tiles, 2048
+    // x 2048 x 8192 97 against 72 us.
     const bool sk_possible = (p.kernel == KERNEL_MFMA_BF16 || p.kernel == KERNEL_MFMA_F16) &&
                              d->batch == 1 && S == 1 && reads_ab(d) && p.tile.per_cu > 0;
-    if (d->schedule == DG_SCHED_STREAM_K && !sk_possible)
+    if (forced_sk && !sk_possible)
         return DG_ERROR_NOT_SUPPORTED;
-    if (sk_possible && d->schedule != DG_SCHED_DATA_PARALLEL) {
+    if (sk_possible && !forbid_sk) {
         const int64_t wave = kNumCu * p.tile.per_cu;     // programs resident at once
         const int64_t iters = ceil_div(d->K, p.tile.bk);
         const int64_t dp = tiles / wave * wave;
@@ -316,7 +377,8 @@ dg_status finish_plan(const dg_gemm_desc *d, Plan p, size_t ws_avail, bool ws_kn
         int64_t splits = R > 0 ? wave / R : 0;
         if (splits > iters / 2) splits = iters / 2;
         if (splits > 16) splits = 16;
-        const bool want = d->schedule == DG_SCHED_STREAM_K || (R * 100 < wave * 85 && d->K >= 2048);
+        const bool want = forced_sk || prefer_sk ||
+                          (dp > 0 && R * 100 < wave * 85 && d->K >= 2048);
         if (R > 0 && splits >= 2 && want) {
             StreamK k{};
             k.dp_tiles = dp;
@@ -325,7 +387,7 @@ dg_status finish_plan(const dg_gemm_desc *d, Plan p, size_t ws_avail, bool ws_kn
             k.tail_splits = ceil_div(d->K, k.k_per_split);   // every slice non-empty
             const size_t ws = (size_t)R * k.tail_splits * p.tile.bm * p.tile.bn * sizeof(float);
             // the automatic choice never asks for more workspace than given
-            if (d->schedule == DG_SCHED_STREAM_K || !ws_known || ws <= ws_avail) {
+            if (forced_sk || !ws_known || ws <= ws_avail) {
                 p.sk = k;
                 p.programs = dp + R * k.tail_splits;
                 p.workspace_bytes = ws;
@@ -345,27 +407,31 @@ dg_status make_plan(const dg_gemm_desc *d, const void *A, const void *B, size_t 
     const int32_t algo = d->algo;
     const TileConfig *table16 = nullptr;   // tiles of the 16-bit matrix-core kernel
     int n16 = 0;
+    const TileConfig *table = nullptr;     // tiles of the chosen family
+    int ntab = 0;
     if (algo == DG_ALGO_MFMA_BF16 || (algo == DG_ALGO_AUTO && mfma16_eligible(d, DG_BF16, A, B))) {
         if (!mfma16_eligible(d, DG_BF16, A, B))
             return DG_ERROR_NOT_SUPPORTED;
         p.kernel = KERNEL_MFMA_BF16;
-        table16 = kMfmaBf16Tiles;
-        n16 = kNumMfmaBf16Tiles;
+        table16 = table = kMfmaBf16Tiles;
+        n16 = ntab = kNumMfmaBf16Tiles;
         p.tile = pick_quantised(d, table16, n16);
     } else if (algo == DG_ALGO_MFMA_F16 ||
                (algo == DG_ALGO_AUTO && mfma16_eligible(d, DG_F16, A, B))) {
         if (!mfma16_eligible(d, DG_F16, A, B))
             return DG_ERROR_NOT_SUPPORTED;
         p.kernel = KERNEL_MFMA_F16;
-        table16 = kMfmaF16Tiles;
-        n16 = kNumMfmaF16Tiles;
+        table16 = table = kMfmaF16Tiles;
+        n16 = ntab = kNumMfmaF16Tiles;
         p.tile = pick_quantised(d, table16, n16);
     } else if (algo == DG_ALGO_MFMA_F32 || (algo == DG_ALGO_AUTO && valu_eligible(d, A, B))) {
         // fp32 on the matrix cores: same operand requirements as the VALU kernel
         if (!valu_eligible(d, A, B))
             return DG_ERROR_NOT_SUPPORTED;
         p.kernel = KERNEL_MFMA_F32;
-        p.tile = pick_quantised(d, kMfmaF32Tiles, kNumMfmaF32Tiles);
+        table = kMfmaF32Tiles;
+        ntab = kNumMfmaF32Tiles;
+        p.tile = pick_quantised(d, table, ntab);
     } else if (algo == DG_ALGO_VALU_F32) {
         if (!valu_eligible(d, A, B))
             return DG_ERROR_NOT_SUPPORTED;
@@ -380,16 +446,25 @@ dg_status make_plan(const dg_gemm_desc *d, const void *A, const void *B, size_t 
     // wave instead (automatic choice, workspace given), the large tile with
     // its better flop-per-byte ratio wins: 4352 x 4352 x 8192 (bf16) ran
     // 295 us that way against 415 us on 128 x 128 tiles.
+    const TunedEntry *tuned = nullptr;
+    if (table && !forced_tile(table, ntab))
+        tuned = find_tuned(d, p.kernel, table, ntab);
+    if (tuned) {
+        p.tile = *tile_named(table, ntab, tuned->tile);
+        p.tuned = 1;
+        return finish_plan(d, p, ws_avail, ws_known, tuned->schedule, tuned->splits, plan);
+    }
     if (table16 && !forced_tile(table16, n16) && p.tile.bm != table16[0].bm) {
         Plan big = p;
         big.tile = table16[0];
         Plan done;
-        if (finish_plan(d, big, ws_avail, ws_known, &done) == DG_SUCCESS && done.sk.tail_tiles > 0) {
+        if (finish_plan(d, big, ws_avail, ws_known, 0, 0, &done) == DG_SUCCESS &&
+            done.sk.tail_tiles > 0) {
             *plan = done;
             return DG_SUCCESS;
         }
     }
-    return finish_plan(d, p, ws_avail, ws_known, plan);
+    return finish_plan(d, p, ws_avail, ws_known, 0, 0, plan);
 }
 
 void fill_args(const dg_gemm_desc *d, const Plan &p, const void *A, const void *B, void *C,
@@ -507,11 +582,12 @@ dg_status dg_gemm_describe(const dg_gemm_desc *d, size_t workspace_bytes, char *
     snprintf(buf, len,
              "kernel=%s tile=%s bm=%d bn=%d bk=%d threads=%d splits=%d k_per_split=%lld "
              "programs=%lld group_m=%d xcd_remap=%d workspace=%zu reduce_blocks=%lld "
-             "fixup_blocks=%lld schedule=%s",
+             "fixup_blocks=%lld tuned=%d schedule=%s",
              kernel_name(p.kernel), p.tile.name, p.tile.bm, p.tile.bn, p.tile.bk, p.tile.threads,
              p.splits, (long long)p.k_per_split, (long long)p.programs,
              d->group_m > 0 ? d->group_m : kDefaultGroupM, d->xcd_remap >= 0 ? 1 : 0,
-             p.workspace_bytes, (long long)p.reduce_blocks, (long long)p.fixup_blocks, sched);
+             p.workspace_bytes, (long long)p.reduce_blocks, (long long)p.fixup_blocks, p.tuned,
+             sched);
     return DG_SUCCESS;
 }
 

@@ -34,6 +34,7 @@ struct Plan {
     int64_t reduce_blocks;   // grid of the split-K reduction (0 if none)
     StreamK sk;              // sk.tail_tiles > 0: stream-K launch
     int64_t fixup_blocks;    // grid of the stream-K fix-up (0 if none)
+    int32_t tuned;           // 1: tile and schedule from the offline-tuned table
 };
 
 // Launchers: enqueue the kernel on `stream`; return hipSuccess or the

@@ -104,9 +104,10 @@ typedef enum {
  * atomics) and applies the epilogue.  STREAM_K applies to the bf16 and fp16
  * matrix-core kernels with batch == 1 and split_k <= 1 and needs workspace
  * (see dg_gemm_workspace_size); otherwise DG_ERROR_NOT_SUPPORTED.  The
- * automatic choice uses it only for those kernels, when the last wave of
- * tiles would be less than 85 % full, K >= 2048 and the caller passes
- * enough workspace. */
+ * automatic choice uses it only for those kernels, when there is at least
+ * one full wave of tiles, the last wave would be less than 85 % full,
+ * K >= 2048 and the caller passes enough workspace, or where the
+ * offline-tuned plan table names it for the exact shape. */
 typedef enum {
     DG_SCHED_AUTO = 0,
     DG_SCHED_DATA_PARALLEL = 1,
@@ -195,7 +196,11 @@ dg_status dg_gemm(const dg_gemm_desc *d, const void *A, const void *B, void *C,
 /* Write a one-line, NUL-terminated description of the plan dg_gemm would
  * run for `d` (kernel, tile, split, grid, workspace) into buf[len].  Pass
  * workspace_bytes as dg_gemm would receive it (it decides split-K when
- * split_k == 0). */
+ * split_k == 0).  "tuned=1" marks a plan taken from the library's
+ * offline-tuned table: for the exact (kernel family, M, N, K, batch) of a
+ * shape swept on an MI355X, the tile and schedule that measured fastest
+ * replace the heuristic choice ("GEMM Kernel Optimization", Autotuning,
+ * with the benchmarking done once, offline). */
 dg_status dg_gemm_describe(const dg_gemm_desc *d, size_t workspace_bytes, char *buf,
                            size_t len);
 

@@ -169,7 +169,9 @@ def _desc_for(p, **kw):
     return dg.make_desc(**f)
 
 
-def test_plans_of_the_five_workloads():
+def test_plans_of_the_five_workloads(monkeypatch):
+    # the heuristic plans (the offline-tuned table switched off)
+    monkeypatch.setenv("DG_TUNED", "0")
     c1 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c1"]))
     assert "kernel=mfma_f32" in c1 and "splits=1" in c1 and "bm=128" in c1
     c2 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c2"]))
@@ -187,6 +189,14 @@ def test_plans_of_the_five_workloads():
     assert "kernel=mfma_bf16" in c5 and "splits=1 " not in c5
     # without workspace the automatic choice does not split
     assert "splits=1 " in dg.dg_gemm_describe(d5, 0)
+    # the tuned plan of the ragged GELU GEMM: 128 x 256 tiles, stream-K
+    # when workspace is given, data-parallel on the same tile without
+    monkeypatch.delenv("DG_TUNED")
+    d4 = _desc_for(W.WORKLOADS["c4"])
+    t4 = dg.dg_gemm_describe(d4, dg.dg_gemm_workspace_size(d4))
+    assert "tuned=1" in t4 and "bm=128 bn=256" in t4 and "schedule=stream_k" in t4
+    t4 = dg.dg_gemm_describe(d4, 0)
+    assert "tuned=1" in t4 and "bm=128 bn=256" in t4 and "schedule=data_parallel" in t4
 
 
 def test_f16_plans():
@@ -250,8 +260,10 @@ def _sk_fields(text):
     return {k: int(kv[k]) for k in ("dp_tiles", "tail_tiles", "tail_splits", "tail_k_per_split")}
 
 
-def test_stream_k_plan_for_a_badly_quantised_grid():
-    # the GELU workload's grid with a long K (the automatic choice wants K >= 2048)
+def test_stream_k_plan_for_a_badly_quantised_grid(monkeypatch):
+    # the heuristic (tuned table off) on the GELU workload's grid with a long
+    # K (the automatic choice wants K >= 2048)
+    monkeypatch.setenv("DG_TUNED", "0")
     d = _desc_for(W.WORKLOADS["c4"].replace(K=4096))
     ws = dg.dg_gemm_workspace_size(d)
     text = dg.dg_gemm_describe(d, ws)
@@ -302,3 +314,39 @@ def test_stream_k_requirements():
     # data-parallel on request
     d4 = _desc_for(W.WORKLOADS["c4"], schedule=dg.DG_SCHED_DATA_PARALLEL)
     assert "schedule=data_parallel" in dg.dg_gemm_describe(d4, 1 << 34)
+
+
+def _tuned_entries():
+    import re
+    path = os.path.join(ROOT, "dense_gemm_10_amd", "csrc", "tuned_table.inc")
+    text = open(path).read()
+    pat = (r'\{(KERNEL_\w+), (\d+), (\d+), (\d+), (\d+), "([\w]+)", (DG_SCHED_\w+), '
+           r'(\d+)\},')
+    return [(k, int(M), int(N), int(K), int(b), t, s, int(S)) for k, M, N, K, b, t, s, S in
+            re.findall(pat, text)]
+
+
+def test_tuned_table_entries_are_what_the_planner_picks(monkeypatch):
+    import itertools
+    from dense_gemm_10_amd.tune import shapes
+    by_shape = {(p.M, p.N, p.K, p.batch, p.a_type): p for p in shapes()}
+    fam_type = {"KERNEL_MFMA_BF16": "bf16", "KERNEL_MFMA_F16": "f16", "KERNEL_MFMA_F32": "f32"}
+    entries = _tuned_entries()
+    for kern, M, N, K, b, tile, sched, splits in entries:
+        p = by_shape[(M, N, K, b, fam_type[kern])]        # every entry comes from a swept shape
+        d = _desc_for(p)
+        ws = dg.dg_gemm_workspace_size(d)
+        text = dg.dg_gemm_describe(d, ws)
+        assert "tuned=1" in text and f"tile={tile} " in text, (p.name, text)
+        if sched == "DG_SCHED_DATA_PARALLEL":
+            assert "schedule=data_parallel" in text
+        if splits:
+            assert f"splits={splits} " in text
+        # DG_TUNED=0 gives the heuristic plan, DG_FORCE_TILE overrides the table
+        monkeypatch.setenv("DG_TUNED", "0")
+        assert "tuned=0" in dg.dg_gemm_describe(d, ws)
+        monkeypatch.delenv("DG_TUNED")
+    # a shape next to a tuned one is not matched
+    for kern, M, N, K, b, tile, sched, splits in itertools.islice(entries, 3):
+        p = by_shape[(M, N, K, b, fam_type[kern])].replace(K=K + 8)
+        assert "tuned=0" in dg.dg_gemm_describe(_desc_for(p), 1 << 34)

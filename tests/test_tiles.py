@@ -1,0 +1,64 @@
+"""GPU parity of every tile configuration of every matrix-core family (the
+candidates the offline tuning sweep may put in the planner's table), under
+the data-parallel and the stream-K schedule, on ragged shapes with a
+partial last K tile, against the CPU oracle."""
+import pytest
+
+import dense_gemm_10_amd as dg
+import oracle
+import workloads as W
+from dense_gemm_10_amd.tune import TILES
+from parity_util import check
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _problem(family, epilogue):
+    dt = {"mfma_bf16": W.BF16, "mfma_f16": W.F16, "mfma_f32": W.F32}[family]
+    if dt == W.F32:
+        base = dict(M=520, N=392, K=300, a_type=dt, b_type=dt, c_type=W.F32)
+    else:
+        base = dict(M=520, N=392, K=1000, a_type=dt, b_type=dt, a_order=W.ROW, b_order=W.COL,
+                    c_type=dt)
+    if epilogue:
+        base.update(c_type=W.F32, alpha=1.5, beta=0.5, has_bias=True, bias_type=dt,
+                    act=W.ACT_GELU_ERF, N=392 - 5)
+        if dt == W.F32:
+            base.update(ldb=392)     # row-major B: the fp32 kernels need ldb % 4 == 0
+    return W.Problem(name=f"{family}_{'epi' if epilogue else 'plain'}", seed=61, **base)
+
+
+CASES = [(f, t, s) for f, tiles in TILES.items() for t in tiles for s in (1, 2)]
+
+
+@pytest.mark.parametrize("family,tile,schedule", CASES,
+                         ids=[f"{t}-{'dp' if s == 1 else 'sk'}" for _, t, s in CASES])
+@pytest.mark.parametrize("epilogue", [False, True])
+def test_every_tile(family, tile, schedule, epilogue, monkeypatch):
+    from workloads.device import DeviceProblem
+    monkeypatch.setenv("DG_FORCE_TILE", tile)
+    p = _problem(family, epilogue)
+    d = dg.make_desc(**dict(W.desc_fields(p), schedule=schedule))
+    try:
+        dg.dg_gemm_describe(d, 1 << 34)
+    except dg.DgError as e:
+        assert schedule == 2 and e.status == dg.DG_ERROR_NOT_SUPPORTED   # fp32: no stream-K
+        pytest.skip("stream-K does not apply to this family")
+    for small_int in (True, False):
+        x = W.make_inputs(p, small_int=small_int)
+        dp = DeviceProblem(p, x, schedule=schedule)
+        text = dp.describe()
+        print(f"[{p.name}] {text}", flush=True)
+        assert f"tile={tile} " in text
+        assert ("schedule=stream_k" in text) == (schedule == 2)
+        dp.run()
+        ref, mag, out = oracle.gemm(p, x.A, x.B, x.C, x.bias)
+        check(p, dp.result(), ref, mag, out, exact=small_int and p.act == W.ACT_NONE,
+              what=f"{tile} sched={schedule} int={small_int}")
