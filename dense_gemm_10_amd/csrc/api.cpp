@@ -231,7 +231,8 @@ struct TunedEntry {
     int64_t M, N, K, batch;
     const char *tile;
     int32_t schedule;     // DG_SCHED_DATA_PARALLEL or DG_SCHED_STREAM_K
-    int32_t splits;       // split-K slices; 0: the automatic choice
+    int32_t splits;       // split-K slices (data-parallel) or K slices per tail
+                          // tile (stream-K); 0: the automatic choice
 };
 
 const TunedEntry kTuned[] = {
@@ -308,7 +309,9 @@ int32_t auto_splits(const dg_gemm_desc *d, int64_t tiles)
 // chosen.  `tuned_sched` and `tuned_splits` are what a tuned entry states
 // (0 if none): they apply where the caller leaves the choice to the
 // library, and like the automatic choice they never ask for more workspace
-// than given.
+// than given.  Under stream-K, a split count (the caller's split_k > 1
+// with a forced stream-K schedule, or the tuned one) is the number of K
+// slices of each tail tile.
 dg_status finish_plan(const dg_gemm_desc *d, Plan p, size_t ws_avail, bool ws_known,
                       int32_t tuned_sched, int32_t tuned_splits, Plan *plan)
 {
@@ -319,13 +322,18 @@ dg_status finish_plan(const dg_gemm_desc *d, Plan p, size_t ws_avail, bool ws_kn
                            (lib_sched && tuned_sched == DG_SCHED_DATA_PARALLEL);
     const int64_t tiles = tiles_of(d, p.tile);
     const int64_t plane = d->batch * d->M * d->N * (int64_t)sizeof(float);
+    int32_t slices = 0;      // requested K slices per stream-K tail tile
+    if (forced_sk && d->split_k > 1)
+        slices = d->split_k;
+    else if (prefer_sk && d->split_k == 0 && tuned_splits > 1)
+        slices = tuned_splits;
     int32_t S;
     if (!reads_ab(d)) {
         S = 1;
+    } else if (forced_sk || (prefer_sk && d->split_k == 0)) {
+        S = 1;   // stream-K asked for: no split-K
     } else if (d->split_k >= 1) {
         S = d->split_k;
-    } else if (forced_sk || prefer_sk) {
-        S = 1;   // stream-K asked for: no automatic split-K
     } else {
         S = tuned_splits > 0 ? tuned_splits : auto_splits(d, tiles);
         // the automatic choice never asks for more workspace than given
@@ -377,6 +385,8 @@ dg_status finish_plan(const dg_gemm_desc *d, Plan p, size_t ws_avail, bool ws_kn
         int64_t splits = R > 0 ? wave / R : 0;
         if (splits > iters / 2) splits = iters / 2;
         if (splits > 16) splits = 16;
+        if (slices > 0)
+            splits = slices < iters ? slices : iters;     // at least one K step each
         const bool want = forced_sk || prefer_sk ||
                           (dp > 0 && R * 100 < wave * 85 && d->K >= 2048);
         if (R > 0 && splits >= 2 && want) {

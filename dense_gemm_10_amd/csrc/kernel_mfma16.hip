@@ -178,6 +178,15 @@ __device__ __forceinline__ int swizzle_key(int r)
     return (r / (16 / CPR)) % CPR;
 }
 
+// LDS of one workgroup: the stage ring, or the epilogue's chunk and bias
+// when those are larger (short rings of wide tiles).
+constexpr int mfma16_lds_bytes(int BM, int BN, int NS, int BK)
+{
+    return NS * (BM + BN) * (BK / 8) * 16 > epilogue_lds_bytes(BN)
+               ? NS * (BM + BN) * (BK / 8) * 16
+               : epilogue_lds_bytes(BN);
+}
+
 // One output tile (or, for stream-K, one K range of it): K loop over
 // [kb, ke) and the epilogue, or the raw fp32 accumulators written to `part`
 // (a BM x BN row-major slot) when `part` is not null.
@@ -410,8 +419,6 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
         barrier();
     }
 
-    static_assert(epilogue_lds_bytes(BN) <= kStages * STAGE_SLOTS * 16,
-                  "epilogue chunk and bias fit in LDS");
     if (part)
         tile_epilogue_rows<BM, BN, WM, WN, true, DT_F32>(g, (char *)part, BN, BM, BN, n0,
                                                          (float *)lds, acc);
@@ -470,7 +477,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f16_kernel(GemmArgs g)
 template <int T, int BM, int BN, int WM, int WN, int NS, int BK>
 hipError_t launch_one(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
-    const size_t lds_bytes = (size_t)NS * (BM + BN) * (BK / 8) * sizeof(uint4);
+    const size_t lds_bytes = (size_t)mfma16_lds_bytes(BM, BN, NS, BK);
     const dim3 grid((unsigned)p.programs), block(64 * WM * WN);
     if constexpr (T == DT_F16)
         hipLaunchKernelGGL((gemm_mfma_f16_kernel<BM, BN, WM, WN, NS, BK>), grid, block, lds_bytes,
@@ -484,6 +491,11 @@ hipError_t launch_one(const GemmArgs &g, const Plan &p, hipStream_t stream)
 } // namespace
 
 // variant index -> instantiation (BM x BN tile, WM x WN wavefronts, ring depth)
+// The last field is the number of workgroups one CU holds at once: the
+// smaller of 160 KB over the workgroup's LDS (ring or epilogue chunk) and
+// 512 registers per SIMD lane over one wave's VGPRs + AccVGPRs (each
+// workgroup puts one wave on each SIMD): 368 for 256 x 256, 196 for
+// 128 x 256 and 256 x 128, 120 for 128 x 128.
 // Entries 0 and 1 are the large and small tiles of the automatic choice:
 // 256 x 256 with whole-line (BK = 64) stages in a 2-stage ring, and
 // 128 x 128 with BK = 32 in a 4-stage ring (64 KB of LDS, two workgroups
@@ -494,12 +506,14 @@ const TileConfig kMfmaBf16Tiles[] = {
     {128, 128, 32, 256, 1, "mfma_bf16_128x128x32_w2x2_s4", 2},
     {256, 256, 32, 256, 0, "mfma_bf16_256x256x32_w2x2_s4", 1},
     {256, 128, 32, 256, 2, "mfma_bf16_256x128x32_w2x2_s4", 1},
-    {256, 128, 32, 256, 3, "mfma_bf16_256x128x32_w2x2_s3", 1},
-    {128, 256, 32, 256, 4, "mfma_bf16_128x256x32_w2x2_s3", 1},
+    {256, 128, 32, 256, 3, "mfma_bf16_256x128x32_w2x2_s3", 2},
+    {128, 256, 32, 256, 4, "mfma_bf16_128x256x32_w2x2_s3", 2},
     {128, 128, 64, 256, 6, "mfma_bf16_128x128x64_w2x2_s3", 1},
     {256, 128, 64, 256, 7, "mfma_bf16_256x128x64_w2x2_s3", 1},
+    {128, 256, 32, 256, 8, "mfma_bf16_128x256x32_w2x2_s2", 2},
+    {128, 128, 32, 256, 9, "mfma_bf16_128x128x32_w2x2_s2", 4},
 };
-const int kNumMfmaBf16Tiles = 8;
+const int kNumMfmaBf16Tiles = 10;
 
 const TileConfig kMfmaF16Tiles[] = {
     {256, 256, 64, 256, 5, "mfma_f16_256x256x64_w2x2_s2", 1},
@@ -525,6 +539,8 @@ hipError_t launch_mfma16(const GemmArgs &g, const Plan &p, hipStream_t stream)
     case 5: return launch_one<DT_BF16, 256, 256, 2, 2, 2, 64>(g, p, stream);
     case 6: return launch_one<DT_BF16, 128, 128, 2, 2, 3, 64>(g, p, stream);
     case 7: return launch_one<DT_BF16, 256, 128, 2, 2, 3, 64>(g, p, stream);
+    case 8: return launch_one<DT_BF16, 128, 256, 2, 2, 2, 32>(g, p, stream);
+    case 9: return launch_one<DT_BF16, 128, 128, 2, 2, 2, 32>(g, p, stream);
     default: return hipErrorInvalidValue;
     }
 }

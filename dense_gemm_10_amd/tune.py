@@ -4,8 +4,9 @@
 
 For every shape below, every tile configuration of the kernel family the
 library picks for it is timed under both schedules (data-parallel and
-stream-K, where stream-K applies) and, where the output tiles alone fill
-less than a wave of the 256 compute units, with 2 to 16 split-K slices,
+stream-K, where stream-K applies, with its own and 4, 8 or 16 K slices per
+tail tile) and, where the output tiles alone fill less than a wave of the
+256 compute units, with 2 to 16 split-K slices,
 next to the library's own heuristic plan
 (timed with the table switched off, DG_TUNED=0).  This is the per-size
 benchmark-and-keep-the-fastest of "GEMM Kernel Optimization" (Autotuning)
@@ -42,7 +43,8 @@ TILES = {
     "mfma_bf16": ["mfma_bf16_256x256x64_w2x2_s2", "mfma_bf16_128x128x32_w2x2_s4",
                   "mfma_bf16_256x256x32_w2x2_s4", "mfma_bf16_256x128x32_w2x2_s4",
                   "mfma_bf16_256x128x32_w2x2_s3", "mfma_bf16_128x256x32_w2x2_s3",
-                  "mfma_bf16_128x128x64_w2x2_s3", "mfma_bf16_256x128x64_w2x2_s3"],
+                  "mfma_bf16_128x128x64_w2x2_s3", "mfma_bf16_256x128x64_w2x2_s3",
+                  "mfma_bf16_128x256x32_w2x2_s2", "mfma_bf16_128x128x32_w2x2_s2"],
     "mfma_f16": ["mfma_f16_256x256x64_w2x2_s2", "mfma_f16_128x128x32_w2x2_s4"],
     "mfma_f32": ["mfma_f32_256x256x16_w2x2", "mfma_f32_128x128x16_w2x2"],
 }
@@ -151,6 +153,16 @@ def sweep(p, steps, log):
             if sched == "stream_k" and sk_kind != "stream_k":
                 continue
             res["cands"].append((tile, sched, 0, t.time(d, ws)))
+            if sched == "stream_k":
+                # other K-slice counts of the tail tiles
+                seen = {_kv(text)["tail_splits"]}
+                for S in (4, 8, 16):
+                    text, d, ws = t.plan(tile=tile, schedule=2, split_k=S)
+                    if text is None or _kv(text).get("tail_splits") in seen:
+                        continue
+                    seen.add(_kv(text)["tail_splits"])
+                    res["cands"].append((tile, sched, S, t.time(d, ws)))
+                continue
             if sched != "data_parallel" or p.split_k:
                 continue
             # explicit split-K counts when the tiles leave compute units idle
@@ -184,8 +196,9 @@ def write_table(results, path, steps, device):
         f"{time.strftime('%Y-%m-%d')}: best of three",
         f"// means of {steps} calls per candidate, CUDA-event timed; an entry replaces the",
         f"// heuristic's plan only when faster by more than {MARGIN:.0%}, otherwise it pins it.",
-        "// Fields: family, M, N, K, batch, tile, schedule, split-K slices (0: automatic).",
-        "// Candidates: tile/schedule (dp, sk; sN for N split-K slices) and microseconds.",
+        "// Fields: family, M, N, K, batch, tile, schedule, slices (0: automatic; split-K",
+        "// slices under data-parallel, K slices per tail tile under stream-K).",
+        "// Candidates: tile/schedule (dp, sk; sN for N slices) and microseconds.",
     ]
     for r in results:
         p = r["problem"]

@@ -101,8 +101,10 @@ typedef enum {
  * data-parallel, and the K range of each remaining (tail) tile is cut into
  * slices, one workgroup each, enough to fill one more wave; a second, small
  * kernel adds each tail tile's fp32 partials in slice order (fixed order, no
- * atomics) and applies the epilogue.  STREAM_K applies to the bf16 and fp16
- * matrix-core kernels with batch == 1 and split_k <= 1 and needs workspace
+ * atomics) and applies the epilogue; with STREAM_K, split_k = S > 1 cuts
+ * each tail tile's K range into slices of ceil(K / S) rounded up to whole K
+ * steps (so possibly fewer than S slices) instead of a split-K count.  STREAM_K applies to the bf16 and fp16 matrix-core
+ * kernels with batch == 1 and needs workspace
  * (see dg_gemm_workspace_size); otherwise DG_ERROR_NOT_SUPPORTED.  The
  * automatic choice uses it only for those kernels, when there is at least
  * one full wave of tiles, the last wave would be less than 85 % full,
@@ -140,7 +142,8 @@ typedef enum {
  *   act             activation, see dg_act.
  *   split_k         0: the library decides (it only splits K when the
  *                   caller passes enough workspace); 1: never split;
- *                   S > 1: split K into S slices (needs workspace).
+ *                   S > 1: split K into S slices (needs workspace); with
+ *                   schedule STREAM_K, the K slices of each tail tile.
  *   group_m         output-tile group height of the swizzled tile order; 0
  *                   picks the default (8).  1 gives plain row-major order.
  *   algo            dg_algo; 0 = automatic choice.

@@ -294,12 +294,20 @@ def test_stream_k_slices_cover_k_once():
 
 def test_stream_k_requirements():
     sk = dict(schedule=dg.DG_SCHED_STREAM_K)
-    # only the bf16 matrix-core kernel, one matrix, no split-K
-    for bad in [_desc(**sk), _desc(a_type="bf16", b_order="col", batch=2, **sk),
-                _desc(a_type="bf16", b_order="col", K=4096, split_k=4, **sk)]:
+    # only the 16-bit matrix-core kernels, one matrix
+    for bad in [_desc(**sk), _desc(a_type="bf16", b_order="col", batch=2, **sk)]:
         with pytest.raises(dg.DgError) as e:
             dg.dg_gemm_describe(bad, 1 << 30)
         assert e.value.status == dg.DG_ERROR_NOT_SUPPORTED
+    # under stream-K, split_k sets the K slices of each tail tile (one K step
+    # at least each): 3000 x 3000 in 256 x 256 tiles is 144 tiles, all in the
+    # tail
+    for S, want in [(4, 4), (8, 8), (100, 64)]:              # K = 4096 is 64 K steps of 64
+        t = dg.dg_gemm_describe(_desc(M=3000, N=3000, K=4096, a_type="bf16", b_order="col",
+                                      split_k=S, **sk), 1 << 34)
+        kv = _sk_fields(t)
+        assert "splits=1 " in t and "bm=256" in t, t
+        assert kv["tail_splits"] == want and kv["tail_tiles"] == 144, t
     d = _desc(M=3000, N=3000, K=256, a_type="bf16", b_order="col", **sk)
     need = dg.dg_gemm_workspace_size(d)
     assert need > 0

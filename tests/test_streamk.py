@@ -116,3 +116,16 @@ def test_stream_k_is_deterministic():
         dp.reset_c()
         dp.run()
         assert np.array_equal(dp.result().view(np.uint8), first.view(np.uint8))
+
+
+# explicit K-slice counts of the tail tiles (split_k under the stream-K
+# schedule), including counts that do not divide K
+@pytest.mark.parametrize("slices", [3, 5, 16])
+def test_stream_k_explicit_slices(slices):
+    p = _bf16(f"sk_slices{slices}", 640, 640 - 3, 1000, split_k=slices)
+    text = _check_full(p, True, schedule=SK)
+    # slices of ceil(K / S) rounded up to whole K steps: 5 slices of K = 1000
+    # in steps of 64 are 256 long, so 4 of them cover K
+    bk = int(dict(t.split("=", 1) for t in text.split() if "=" in t)["bk"])
+    kps = -(-(-(-1000 // slices)) // bk) * bk
+    assert "splits=1 " in text and _tail(text)[1] == -(-1000 // kps)
