@@ -189,14 +189,17 @@ def test_plans_of_the_five_workloads(monkeypatch):
     assert "kernel=mfma_bf16" in c5 and "splits=1 " not in c5
     # without workspace the automatic choice does not split
     assert "splits=1 " in dg.dg_gemm_describe(d5, 0)
-    # the tuned plan of the ragged GELU GEMM: 128 x 256 tiles, stream-K
+    # the tuned plan of the ragged GELU GEMM: the table's tile with stream-K
     # when workspace is given, data-parallel on the same tile without
     monkeypatch.delenv("DG_TUNED")
-    d4 = _desc_for(W.WORKLOADS["c4"])
+    p4 = W.WORKLOADS["c4"]
+    entry = [e for e in _tuned_entries() if e[:5] == ("KERNEL_MFMA_BF16", p4.M, p4.N, p4.K, 1)]
+    assert len(entry) == 1 and entry[0][6] == "DG_SCHED_STREAM_K"
+    d4 = _desc_for(p4)
     t4 = dg.dg_gemm_describe(d4, dg.dg_gemm_workspace_size(d4))
-    assert "tuned=1" in t4 and "bm=128 bn=256" in t4 and "schedule=stream_k" in t4
+    assert "tuned=1" in t4 and f"tile={entry[0][5]} " in t4 and "schedule=stream_k" in t4
     t4 = dg.dg_gemm_describe(d4, 0)
-    assert "tuned=1" in t4 and "bm=128 bn=256" in t4 and "schedule=data_parallel" in t4
+    assert "tuned=1" in t4 and f"tile={entry[0][5]} " in t4 and "schedule=data_parallel" in t4
 
 
 def test_f16_plans():
