@@ -354,7 +354,7 @@ dg_status finish_plan(const dg_gemm_desc *d, Plan p, size_t ws_avail, bool ws_kn
     p.programs = programs;
     if (S > 1) {
         int64_t total = d->batch * d->M * d->N;
-        int64_t blocks = ceil_div(total, 256);
+        int64_t blocks = ceil_div(total, reduce_by_four(d->N, total) ? 1024 : 256);
         p.reduce_blocks = blocks < 65536 ? blocks : 65536;
     }
 

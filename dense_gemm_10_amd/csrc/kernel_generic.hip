@@ -130,6 +130,32 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int32_t 
     }
 }
 
+// The same reduction, four consecutive outputs of one row per thread, when
+// N is a multiple of 4 and the batch's outputs fit 32-bit indices: one
+// 16-byte read per split and per thread, and 32-bit row / column math.
+__global__ __launch_bounds__(256) void splitk_reduce4_kernel(GemmArgs g, int32_t splits)
+{
+    const uint32_t total = (uint32_t)(g.sched.batch * g.M * g.N);
+    const uint32_t N = (uint32_t)g.N, M = (uint32_t)g.M;
+    for (uint32_t e = (blockIdx.x * 256u + threadIdx.x) * 4u; e < total;
+         e += gridDim.x * 1024u) {
+        float4 sum = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int32_t s = 0; s < splits; ++s) {
+            const float4 v = *(const float4 *)(g.ws + (int64_t)s * total + e);
+            sum.x += v.x;
+            sum.y += v.y;
+            sum.z += v.z;
+            sum.w += v.w;
+        }
+        const uint32_t row = e / N, n = e - row * N;
+        const uint32_t b = row / M, m = row - b * M;
+        const float acc[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            store_c(g, b, m, n + j, epilogue_value(g, b, m, n + j, acc[j]));
+    }
+}
+
 // Stream-K fix-up: each tail tile left tail_splits fp32 partials in the
 // workspace, one per K slice; add them in slice order (a fixed order, so
 // the result is reproducible) and apply the epilogue once.
@@ -192,7 +218,10 @@ hipError_t launch_streamk_fixup(const GemmArgs &g, const Plan &p, hipStream_t st
 hipError_t launch_splitk_reduce(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
     dim3 grid((unsigned)p.reduce_blocks), block(256);
-    hipLaunchKernelGGL(splitk_reduce_kernel, grid, block, 0, stream, g, p.splits);
+    if (reduce_by_four(g.N, g.sched.batch * g.M * g.N))
+        hipLaunchKernelGGL(splitk_reduce4_kernel, grid, block, 0, stream, g, p.splits);
+    else
+        hipLaunchKernelGGL(splitk_reduce_kernel, grid, block, 0, stream, g, p.splits);
     return hipGetLastError();
 }
 

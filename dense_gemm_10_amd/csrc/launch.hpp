@@ -37,6 +37,13 @@ struct Plan {
     int32_t tuned;           // 1: tile and schedule from the offline-tuned table
 };
 
+// Whether the split-K reduction takes four outputs per thread (N a multiple
+// of 4, every output index below 2^31); its grid is then a quarter as large.
+inline bool reduce_by_four(int64_t N, int64_t total)
+{
+    return N % 4 == 0 && total < ((int64_t)1 << 31);
+}
+
 // Launchers: enqueue the kernel on `stream`; return hipSuccess or the
 // launch error.
 hipError_t launch_generic(const GemmArgs &g, const Plan &p, hipStream_t stream);

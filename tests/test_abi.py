@@ -156,7 +156,10 @@ def test_forced_split_needs_workspace():
     d = _desc(K=4096, split_k=4)
     need = dg.dg_gemm_workspace_size(d)
     assert need == 4 * 64 * 48 * 4
-    assert "reduce_blocks=12 " in dg.dg_gemm_describe(d, need)     # 64 * 48 outputs / 256
+    # 64 * 48 outputs, N a multiple of 4: four per thread, 1024 per block
+    assert "reduce_blocks=3 " in dg.dg_gemm_describe(d, need)
+    d47 = _desc(K=4096, N=47, ldb=47, ldc=47, split_k=4)            # one output per thread
+    assert "reduce_blocks=12 " in dg.dg_gemm_describe(d47, dg.dg_gemm_workspace_size(d47))
     assert _gemm_status(d) == dg.DG_ERROR_INSUFFICIENT_WORKSPACE
     assert _gemm_status(d, ws=PW, ws_bytes=need - 4) == dg.DG_ERROR_INSUFFICIENT_WORKSPACE
     # workspace overlapping C
