@@ -4,7 +4,7 @@
 // Same tiling as the other kernels ("La GEMM, de zero a cuBLAS", the three
 // tiling levels of section 2.6: workgroup tile in LDS, wave tile in
 // registers, 32 x 32 MFMA blocks), for every operand order:
-//   - tile BM x BN, BK = 16, 4 wavefronts in a 2 x 2 layout; each wave owns
+//   - tile BM x BN, BK = 16 or 32, 4 wavefronts in a 2 x 2 layout; each wave owns
 //     a (BM/2) x (BN/2) tile of 32 x 32 blocks in fp32 accumulators;
 //   - A is staged in LDS as As[k][m] and B as Bs[k][n] (section 2.7's
 //     transposed A), so the operand an MFMA lane needs - row (l mod 32) of
@@ -17,9 +17,10 @@
 //     half-way through it, one barrier per K tile (section 2.8);
 //   - inside a K tile the fragment reads of each k-step are interleaved
 //     with the MFMAs of the previous one.
-// A 32x32x2 fp32 MFMA does 4096 flops in 64 cycles; per 16-deep K tile a
-// wave issues 8 k-steps of FM*FN MFMAs against 8*(FM+FN) one-float LDS
-// reads, so the kernel is bound by the matrix pipe, not by memory.
+// A 32x32x2 fp32 MFMA does 4096 flops in 64 cycles; per BK-deep K tile a
+// wave issues BK/2 k-steps of FM*FN MFMAs against BK/2*(FM+FN) one-float
+// LDS reads, so the kernel is bound by the matrix pipe, not by memory.  A
+// 32-deep K tile halves the barriers and stage hand-offs per K.
 //
 // Requirements checked on the host: fp32 A and B, 16-byte aligned base
 // pointers, lda, ldb and batch strides multiples of 4 elements.
@@ -30,7 +31,6 @@ namespace dg {
 
 namespace {
 
-constexpr int FBK = 16;
 constexpr int FPAD = 4;
 
 // 4 consecutive fp32 at p[off .. off+3]; element j exists iff line_ok &&
@@ -50,9 +50,10 @@ __device__ __forceinline__ float4 load4_masked(const float *p, int64_t off, bool
     return v;
 }
 
-template <int BM, int BN, int WM, int WN, bool A_COL, bool B_COL>
+template <int BM, int BN, int WM, int WN, int FBK, bool A_COL, bool B_COL>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f32_kernel(GemmArgs g)
 {
+    constexpr int KQ = FBK / 4;                            // 128-bit vectors per K-contiguous line
     constexpr int NT = 64 * WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f32_kernel(GemmArgs g)
         if (e < A_VEC) {
             const int idx = tid + e * NT;
             if (!A_COL) {
-                const int r = idx / 4, kq = idx % 4;
+                const int r = idx / KQ, kq = idx % KQ;
                 ra[e] = *(const float4 *)(A + (m0 + r) * lda + k0 + kq * 4);
             } else {
                 const int k = idx / (BM / 4), mq = idx % (BM / 4);
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f32_kernel(GemmArgs g)
                 const int k = idx / (BN / 4), nq = idx % (BN / 4);
                 rb[e - A_VEC] = *(const float4 *)(B + (k0 + k) * ldb + n0 + nq * 4);
             } else {
-                const int n = idx / 4, kq = idx % 4;
+                const int n = idx / KQ, kq = idx % KQ;
                 rb[e - A_VEC] = *(const float4 *)(B + (n0 + n) * ldb + k0 + kq * 4);
             }
         }
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f32_kernel(GemmArgs g)
         for (int e = 0; e < A_VEC; ++e) {
             const int idx = tid + e * NT;
             if (!A_COL) {            // A[m][k] at m*lda + k: 4 k per vector
-                const int r = idx / 4, kq = idx % 4;
+                const int r = idx / KQ, kq = idx % KQ;
                 const int64_t gm = m0 + r, gk = k0 + kq * 4;
                 ra[e] = load4_masked(A, gm * lda + gk, gm < M, gk, ke);
             } else {                 // A[m][k] at k*lda + m: 4 m per vector
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f32_kernel(GemmArgs g)
                 const int64_t gk = k0 + k, gn = n0 + nq * 4;
                 rb[e] = load4_masked(B, gk * ldb + gn, gk < ke, gn, N);
             } else {                 // B[k][n] at n*ldb + k: 4 k per vector
-                const int n = idx / 4, kq = idx % 4;
+                const int n = idx / KQ, kq = idx % KQ;
                 const int64_t gn = n0 + n, gk = k0 + kq * 4;
                 rb[e] = load4_masked(B, gn * ldb + gk, gn < N, gk, ke);
             }
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f32_kernel(GemmArgs g)
         if (e < A_VEC) {
             const int idx = tid + e * NT;
             if (!A_COL) {
-                const int r = idx / 4, kq = idx % 4;
+                const int r = idx / KQ, kq = idx % KQ;
                 as[(kq * 4 + 0) * ALD + r] = ra[e].x;
                 as[(kq * 4 + 1) * ALD + r] = ra[e].y;
                 as[(kq * 4 + 2) * ALD + r] = ra[e].z;
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f32_kernel(GemmArgs g)
                 const int k = idx / (BN / 4), nq = idx % (BN / 4);
                 *(float4 *)&bs[k * BLD + nq * 4] = v;
             } else {
-                const int n = idx / 4, kq = idx % 4;
+                const int n = idx / KQ, kq = idx % KQ;
                 bs[(kq * 4 + 0) * BLD + n] = v.x;
                 bs[(kq * 4 + 1) * BLD + n] = v.y;
                 bs[(kq * 4 + 2) * BLD + n] = v.z;
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f32_kernel(GemmArgs g)
     tile_epilogue<BM, BN, WM, WN>(g, tc, smem, m0, n0, acc);
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int FBK>
 size_t f32_lds_bytes()
 {
     const size_t loop = (size_t)2 * FBK * ((BM + FPAD) + (BN + FPAD)) * sizeof(float);
@@ -282,39 +283,45 @@ size_t f32_lds_bytes()
     return loop > epi ? loop : epi;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int FBK>
 hipError_t launch_f32(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
-    const size_t lds = f32_lds_bytes<BM, BN, WM, WN>();
+    const size_t lds = f32_lds_bytes<BM, BN, WM, WN, FBK>();
     dim3 grid((unsigned)p.programs), block(64 * WM * WN);
     if (!g.a_col && !g.b_col)
-        hipLaunchKernelGGL((gemm_mfma_f32_kernel<BM, BN, WM, WN, false, false>), grid, block, lds,
+        hipLaunchKernelGGL((gemm_mfma_f32_kernel<BM, BN, WM, WN, FBK, false, false>), grid, block, lds,
                            stream, g);
     else if (!g.a_col && g.b_col)
-        hipLaunchKernelGGL((gemm_mfma_f32_kernel<BM, BN, WM, WN, false, true>), grid, block, lds,
+        hipLaunchKernelGGL((gemm_mfma_f32_kernel<BM, BN, WM, WN, FBK, false, true>), grid, block, lds,
                            stream, g);
     else if (g.a_col && !g.b_col)
-        hipLaunchKernelGGL((gemm_mfma_f32_kernel<BM, BN, WM, WN, true, false>), grid, block, lds,
+        hipLaunchKernelGGL((gemm_mfma_f32_kernel<BM, BN, WM, WN, FBK, true, false>), grid, block, lds,
                            stream, g);
     else
-        hipLaunchKernelGGL((gemm_mfma_f32_kernel<BM, BN, WM, WN, true, true>), grid, block, lds,
+        hipLaunchKernelGGL((gemm_mfma_f32_kernel<BM, BN, WM, WN, FBK, true, true>), grid, block, lds,
                            stream, g);
     return hipGetLastError();
 }
 
 } // namespace
 
+// Entries 0 and 1 are the large and small tiles of the automatic choice;
+// the 32-deep ones are selectable by name and by the tuned table.
 const TileConfig kMfmaF32Tiles[] = {
-    {256, 256, FBK, 256, 0, "mfma_f32_256x256x16_w2x2"},
-    {128, 128, FBK, 256, 1, "mfma_f32_128x128x16_w2x2"},
+    {256, 256, 16, 256, 0, "mfma_f32_256x256x16_w2x2"},
+    {128, 128, 16, 256, 1, "mfma_f32_128x128x16_w2x2"},
+    {256, 256, 32, 256, 2, "mfma_f32_256x256x32_w2x2"},
+    {128, 128, 32, 256, 3, "mfma_f32_128x128x32_w2x2"},
 };
-const int kNumMfmaF32Tiles = 2;
+const int kNumMfmaF32Tiles = 4;
 
 hipError_t launch_mfma_f32(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
     switch (p.tile.variant) {
-    case 0: return launch_f32<256, 256, 2, 2>(g, p, stream);
-    case 1: return launch_f32<128, 128, 2, 2>(g, p, stream);
+    case 0: return launch_f32<256, 256, 2, 2, 16>(g, p, stream);
+    case 1: return launch_f32<128, 128, 2, 2, 16>(g, p, stream);
+    case 2: return launch_f32<256, 256, 2, 2, 32>(g, p, stream);
+    case 3: return launch_f32<128, 128, 2, 2, 32>(g, p, stream);
     default: return hipErrorInvalidValue;
     }
 }
