@@ -217,6 +217,21 @@ def collect_profile(workload, tmp, out_dir=PROFILES, knobs=()):
     results["L2"] = {"hits_per_dispatch": hit, "misses_per_dispatch": miss,
                      "hit_rate": hit / (hit + miss) if hit + miss > 0 else None,
                      "command": _shown(cmd, tmp)}
+    # 4. utilisation: matrix-pipe busy share of SIMD cycles, VALU busy share
+    # of CU cycles, LDS bank-conflict cycles per LDS cycle (rocprofv3's
+    # derived metrics; 4 SQ counters and 1 GRBM counter in one pass)
+    out = os.path.join(tmp, "util")
+    cmd = _rocprof(["--pmc", "MfmaUtil", "VALUBusy", "LdsBankConflict"], out) + child + [
+        "--steps", "3", "--warmup", "1"]
+    log(f"[profile] {' '.join(cmd)}")
+    subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL)
+    rows = _csv_rows(out, "counter_collection.csv")
+    util = {}
+    for name in ("MfmaUtil", "VALUBusy", "LdsBankConflict"):
+        sel = [r for r in rows if r["Counter_Name"] == name]
+        util[name] = _per_dispatch(sel, "gemm_")[0] if sel else None
+    util["command"] = _shown(cmd, tmp)
+    results["utilisation"] = util
     results["kernel_source_hash"] = kernel_source_hash()
     results["workload"] = workload
     results["knobs"] = list(knobs)
@@ -256,6 +271,14 @@ def write_profile(results, out_dir=PROFILES):
     lines += ["", f"Commands: `{results['FETCH_SIZE']['command']}`, "
               f"`{results['WRITE_SIZE']['command']}`; calibration: "
               f"`{results['FETCH_SIZE']['copy_command']}`", ""]
+    if "utilisation" in results:
+        u = results["utilisation"]
+        fmt = lambda v, f: "n/a" if v is None else f.format(v)  # noqa: E731
+        lines += ["## Utilisation per GEMM dispatch", "",
+                  "| MfmaUtil (% of SIMD cycles) | VALUBusy (% of CU cycles) | "
+                  "LdsBankConflict (conflict cycles per LDS cycle) |", "|---|---|---|",
+                  f"| {fmt(u['MfmaUtil'], '{:.1f}')} | {fmt(u['VALUBusy'], '{:.1f}')} | "
+                  f"{fmt(u['LdsBankConflict'], '{:.4f}')} |", "", f"Command: `{u['command']}`", ""]
     if "L2" in results:
         l2 = results["L2"]
         lines += ["## L2 (TCC) hit rate per GEMM dispatch", "",
