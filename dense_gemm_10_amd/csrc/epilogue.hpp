@@ -167,6 +167,168 @@ __device__ __forceinline__ void stage_chunk(float *chunk, int c,
     }
 }
 
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
+// Epilogue of a whole tile (all BM x BN outputs inside the output) whose
+// rows all start on a 16-byte boundary: the common interior case of
+// tile_epilogue_rows, with its arithmetic and stores, minus the per-run
+// alignment and edge logic.  Chunk c holds block row c of every wave's
+// accumulators (32 * WM tile rows, so all waves stage each chunk).  Thread
+// t owns one 16-byte column run, the same in every row it stores, and the
+// rows t / RPR + q * (NT / RPR) of each chunk.  The runs are taken in
+// groups whose values fit the registers left beside the accumulators (REGS
+// per lane in all, the budget the kernel was compiled to): all of a group's
+// LDS reads (and C reads when beta != 0) are issued before its first
+// store, so their latencies overlap instead of adding up run after run.
+template <int BM, int BN, int WM, int WN, bool PARTIAL, int OUT, int REGS>
+__device__ __forceinline__ void tile_epilogue_aligned(const GemmArgs &g, char *out, int64_t ld,
+                                                      int64_t n0, float *lds,
+                                                      const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
+{
+    constexpr int NT = 64 * WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int CH_ROWS = 32 * WM;                  // tile rows per chunk
+    constexpr int EP_LD = epilogue_ld(BN);
+    constexpr bool HALF_OUT = OUT != DT_F32;
+    constexpr int VEC = HALF_OUT ? 8 : 4;             // outputs per 16-byte run
+    constexpr int ES = HALF_OUT ? 2 : 4;              // output element size
+    constexpr int RPR = BN / VEC;                     // runs per row
+    constexpr int RSTEP = NT / RPR;                   // chunk rows between a thread's runs
+    constexpr int RUNS = CH_ROWS / RSTEP;             // runs per thread per chunk
+    static_assert(CH_ROWS <= kEpilogueRows, "chunk fits the staging buffer");
+    static_assert(NT % RPR == 0 && 32 % RSTEP == 0 && RUNS * RSTEP == CH_ROWS, "run split");
+    // registers per run in flight (values, and C's when beta != 0); about
+    // 40 more stay with addresses, bias and loop state
+    constexpr int PER_RUN = VEC + (PARTIAL ? 0 : 4);
+    constexpr int SPARE = REGS - BM * BN / NT - 40;
+    constexpr int GROUP = PER_RUN * RUNS <= SPARE ? RUNS
+                        : PER_RUN * (RUNS / 2) <= SPARE ? RUNS / 2
+                        : PER_RUN * (RUNS / 4) <= SPARE ? RUNS / 4 : 1;
+    static_assert(RUNS % GROUP == 0, "groups split the runs");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int frag_half = lane >> 5;
+    const int col = (tid % RPR) * VEC;                // tile column of the thread's run
+    const int rt = tid / RPR;                         // first chunk row of the thread
+    const int64_t ld_bytes = ld * ES;
+    char *base = out + (int64_t)rt * ld_bytes + (int64_t)col * ES;
+    const float *rd = lds + rt * EP_LD + col;
+    float bias[VEC];
+    const bool has_bias = !PARTIAL && g.bias;
+    if (has_bias) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            bias[e] = load_as_f32(g.bias, g.bias_type, n0 + col + e);
+    }
+    const bool read_c = !PARTIAL && g.beta != 0.0f;
+    // Block row I of the wave's accumulators -> chunk rows wm * 32 + [0, 32).
+    auto stage = [&](auto I) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row = wm * 32 + 8 * (v / 4) + 4 * frag_half + (v % 4);
+            float *dst = lds + row * EP_LD + wn * TN + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                dst[j * 32] = acc[decltype(I)::value][j][v];
+        }
+    };
+    // One copy of the chunk code per chunk, each with its chunk index a
+    // constant: a loop over the chunks, unrolled or not, leaves the
+    // accumulators indexed at run time (and so in scratch memory) once its
+    // body - the unrolled runs and their activations - is large.
+    static_for<FM>([&](auto I) {
+        constexpr int c = decltype(I)::value;
+        stage(I);
+        lds_barrier();
+        // chunk row rt + q * RSTEP is tile row (q * RSTEP / 32) * TM + c * 32 + (q * RSTEP) % 32 + rt
+        static_for<RUNS / GROUP>([&](auto G) {
+            constexpr int q0 = decltype(G)::value * GROUP;
+            uint4 cin[GROUP];
+            if (read_c) {
+#pragma unroll
+                for (int u = 0; u < GROUP; ++u) {
+                    const int q = q0 + u;
+                    const int trow = (q * RSTEP / 32) * TM + c * 32 + (q * RSTEP) % 32;
+                    cin[u] = *(const uint4 *)(base + (int64_t)trow * ld_bytes);
+                }
+            }
+            float v[GROUP][VEC];
+#pragma unroll
+            for (int u = 0; u < GROUP; ++u)
+#pragma unroll
+                for (int e = 0; e < VEC; e += 4) {
+                    const float4 x = *(const float4 *)&rd[(q0 + u) * RSTEP * EP_LD + e];
+                    v[u][e] = x.x; v[u][e + 1] = x.y; v[u][e + 2] = x.z; v[u][e + 3] = x.w;
+                }
+            // Each step covers the whole group, so every uniform branch
+            // (beta, bias, activation) is taken once per group, not per run.
+            if (!PARTIAL) {
+#pragma unroll
+                for (int u = 0; u < GROUP; ++u)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        v[u][e] *= g.alpha;
+                if (read_c) {
+#pragma unroll
+                    for (int u = 0; u < GROUP; ++u) {
+                        const uint32_t w[4] = {cin[u].x, cin[u].y, cin[u].z, cin[u].w};
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) {
+                            const float x = HALF_OUT ? half_to_f32<OUT>((uint16_t)(w[e / 2] >> (16 * (e % 2))))
+                                                     : __uint_as_float(w[e]);
+                            v[u][e] = fmaf(g.beta, x, v[u][e]);
+                        }
+                    }
+                }
+                if (has_bias) {
+#pragma unroll
+                    for (int u = 0; u < GROUP; ++u)
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e)
+                            v[u][e] += bias[e];
+                }
+                auto act_all = [&](auto A) {
+#pragma unroll
+                    for (int u = 0; u < GROUP; ++u)
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e)
+                            v[u][e] = activate(v[u][e], decltype(A)::value);
+                };
+                if (g.act == ACT_GELU_ERF)
+                    act_all(std::integral_constant<int32_t, ACT_GELU_ERF>{});
+                else if (g.act == ACT_GELU_TANH)
+                    act_all(std::integral_constant<int32_t, ACT_GELU_TANH>{});
+            }
+#pragma unroll
+            for (int u = 0; u < GROUP; ++u) {
+                const int q = q0 + u;
+                const int trow = (q * RSTEP / 32) * TM + c * 32 + (q * RSTEP) % 32;
+                char *dst = base + (int64_t)trow * ld_bytes;
+                if (HALF_OUT) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        w[e] = (uint32_t)f32_to_half<OUT>(v[u][2 * e]) |
+                               ((uint32_t)f32_to_half<OUT>(v[u][2 * e + 1]) << 16);
+                    *(uint4 *)dst = make_uint4(w[0], w[1], w[2], w[3]);
+                } else {
+                    *(float4 *)dst = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
+                }
+            }
+        });
+        lds_barrier();
+    });
+}
+
 // Epilogue of a tile of a row-major output (C, or the split-K workspace
 // when PARTIAL, fp32), of dtype OUT, at any alignment and with ragged
 // edges.  Each output row is cut into 16-byte aligned runs of VEC elements
@@ -180,7 +342,7 @@ __device__ __forceinline__ void stage_chunk(float *chunk, int c,
 // `out` points at the tile's first element, `ld` is the output's row
 // stride (elements), rows x cols the part of the tile inside the output and
 // n0 the tile's first column (for the bias).
-template <int BM, int BN, int WM, int WN, bool PARTIAL, int OUT>
+template <int BM, int BN, int WM, int WN, bool PARTIAL, int OUT, int REGS = 512>
 __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out, int64_t ld,
                                                    int rows, int cols, int64_t n0, float *lds,
                                                    const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
@@ -201,6 +363,10 @@ __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out,
     const int d0 = (int)(((uintptr_t)out % 16) / ES);
     const int dl = (int)(ld % VEC);
     auto shift = [&](int r) { return (d0 + r * dl) & (VEC - 1); };
+    if (rows == BM && cols == BN && d0 == 0 && dl == 0) {
+        tile_epilogue_aligned<BM, BN, WM, WN, PARTIAL, OUT, REGS>(g, out, ld, n0, lds, acc);
+        return;
+    }
     const bool has_bias = !PARTIAL && g.bias;
     if (has_bias) {
         for (int t = tid; t < BN; t += NT)
@@ -300,7 +466,7 @@ __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out,
 // bytes and no wave may still be reading it for other purposes.  Row-major
 // outputs (and split-K partials) take tile_epilogue_rows; a column-major C
 // goes through store_chunk.
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int REGS = 512>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs &g, const TileCoord &tc, float *lds,
                                               int64_t m0, int64_t n0,
                                               const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
@@ -309,22 +475,22 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs &g, const TileCoord
     const int cols = (int)(g.N - n0 < BN ? g.N - n0 : BN);
     if (g.write_partial) {
         float *out = g.ws + (((int64_t)tc.s * g.sched.batch + tc.b) * g.M + m0) * g.N + n0;
-        tile_epilogue_rows<BM, BN, WM, WN, true, DT_F32>(g, (char *)out, g.N, rows, cols, n0,
+        tile_epilogue_rows<BM, BN, WM, WN, true, DT_F32, REGS>(g, (char *)out, g.N, rows, cols, n0,
                                                          lds, acc);
         return;
     }
     if (!g.c_col) {
         if (g.c_type == DT_F32) {
             char *out = (char *)g.C + (tc.b * g.sc + m0 * g.ldc + n0) * 4;
-            tile_epilogue_rows<BM, BN, WM, WN, false, DT_F32>(g, out, g.ldc, rows, cols, n0, lds,
+            tile_epilogue_rows<BM, BN, WM, WN, false, DT_F32, REGS>(g, out, g.ldc, rows, cols, n0, lds,
                                                               acc);
         } else {
             char *out = (char *)g.C + (tc.b * g.sc + m0 * g.ldc + n0) * 2;
             if (g.c_type == DT_BF16)
-                tile_epilogue_rows<BM, BN, WM, WN, false, DT_BF16>(g, out, g.ldc, rows, cols, n0,
+                tile_epilogue_rows<BM, BN, WM, WN, false, DT_BF16, REGS>(g, out, g.ldc, rows, cols, n0,
                                                                    lds, acc);
             else
-                tile_epilogue_rows<BM, BN, WM, WN, false, DT_F16>(g, out, g.ldc, rows, cols, n0,
+                tile_epilogue_rows<BM, BN, WM, WN, false, DT_F16, REGS>(g, out, g.ldc, rows, cols, n0,
                                                                   lds, acc);
         }
         return;

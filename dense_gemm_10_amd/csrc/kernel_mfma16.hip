@@ -187,6 +187,21 @@ constexpr int mfma16_lds_bytes(int BM, int BN, int NS, int BK)
                : epilogue_lds_bytes(BN);
 }
 
+// Workgroups one CU holds at once: LDS allows 160 KB / mfma16_lds_bytes,
+// and registers 512 per SIMD lane over one wave's (each workgroup puts one
+// wave on each SIMD).  A wave's registers are its BM*BN/256 fp32
+// accumulators plus about as many again for fragments, addresses and the
+// epilogue, so a 256 x 256 tile gets one workgroup per CU, 256 x 128 and
+// 128 x 256 two and 128 x 128 four; the kernels are compiled to that
+// register budget (amdgpu_waves_per_eu) and the planner sizes full waves
+// of stream-K and split-K by it.
+constexpr int mfma16_per_cu(int BM, int BN, int NS, int BK)
+{
+    const int by_lds = 160 * 1024 / mfma16_lds_bytes(BM, BN, NS, BK);
+    const int by_regs = 4 * 128 * 128 / (BM * BN);
+    return by_lds < by_regs ? by_lds : by_regs;
+}
+
 // One output tile (or, for stream-K, one K range of it): K loop over
 // [kb, ke) and the epilogue, or the raw fp32 accumulators written to `part`
 // (a BM x BN row-major slot) when `part` is not null.
@@ -419,11 +434,13 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
         barrier();
     }
 
+    // the epilogue keeps within the kernel's register budget
+    constexpr int REGS = 512 / mfma16_per_cu(BM, BN, kStages, MBK);
     if (part)
-        tile_epilogue_rows<BM, BN, WM, WN, true, DT_F32>(g, (char *)part, BN, BM, BN, n0,
-                                                         (float *)lds, acc);
+        tile_epilogue_rows<BM, BN, WM, WN, true, DT_F32, REGS>(g, (char *)part, BN, BM, BN, n0,
+                                                               (float *)lds, acc);
     else
-        tile_epilogue<BM, BN, WM, WN>(g, tc, (float *)lds, m0, n0, acc);
+        tile_epilogue<BM, BN, WM, WN, REGS>(g, tc, (float *)lds, m0, n0, acc);
 }
 
 // Data-parallel launches give each program one tile (or split-K slice).
@@ -461,14 +478,18 @@ __device__ __forceinline__ void mfma16_program(const GemmArgs &g, uint4 *lds)
 
 // One kernel name per element type, so that traces tell them apart.
 template <int BM, int BN, int WM, int WN, int kStages, int MBK>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_bf16_kernel(GemmArgs g)
+__global__ __launch_bounds__(64 * WM * WN)
+__attribute__((amdgpu_waves_per_eu(mfma16_per_cu(BM, BN, kStages, MBK))))
+void gemm_mfma_bf16_kernel(GemmArgs g)
 {
     extern __shared__ uint4 lds[];
     mfma16_program<DT_BF16, BM, BN, WM, WN, kStages, MBK>(g, lds);
 }
 
 template <int BM, int BN, int WM, int WN, int kStages, int MBK>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f16_kernel(GemmArgs g)
+__global__ __launch_bounds__(64 * WM * WN)
+__attribute__((amdgpu_waves_per_eu(mfma16_per_cu(BM, BN, kStages, MBK))))
+void gemm_mfma_f16_kernel(GemmArgs g)
 {
     extern __shared__ uint4 lds[];
     mfma16_program<DT_F16, BM, BN, WM, WN, kStages, MBK>(g, lds);
@@ -490,35 +511,34 @@ hipError_t launch_one(const GemmArgs &g, const Plan &p, hipStream_t stream)
 
 } // namespace
 
-// variant index -> instantiation (BM x BN tile, WM x WN wavefronts, ring depth)
-// The last field is the number of workgroups one CU holds at once: the
-// smaller of 160 KB over the workgroup's LDS (ring or epilogue chunk) and
-// 512 registers per SIMD lane over one wave's VGPRs + AccVGPRs (each
-// workgroup puts one wave on each SIMD): 368 for 256 x 256, 196 for
-// 128 x 256 and 256 x 128, 120 for 128 x 128.
+// variant index -> instantiation (BM x BN tile, WM x WN wavefronts, ring
+// depth); the last field is mfma16_per_cu of the instantiation.
 // Entries 0 and 1 are the large and small tiles of the automatic choice:
 // 256 x 256 with whole-line (BK = 64) stages in a 2-stage ring, and
 // 128 x 128 with BK = 32 in a 4-stage ring (64 KB of LDS, two workgroups
 // per CU).  The others are selectable by name for sweeps.  The fp16 table
 // holds the two tiles of the automatic choice.
+#define DG_TILE16(T, BM, BN, BK, NS, V) \
+    {BM, BN, BK, 256, V, "mfma_" #T "_" #BM "x" #BN "x" #BK "_w2x2_s" #NS, mfma16_per_cu(BM, BN, NS, BK)}
 const TileConfig kMfmaBf16Tiles[] = {
-    {256, 256, 64, 256, 5, "mfma_bf16_256x256x64_w2x2_s2", 1},
-    {128, 128, 32, 256, 1, "mfma_bf16_128x128x32_w2x2_s4", 2},
-    {256, 256, 32, 256, 0, "mfma_bf16_256x256x32_w2x2_s4", 1},
-    {256, 128, 32, 256, 2, "mfma_bf16_256x128x32_w2x2_s4", 1},
-    {256, 128, 32, 256, 3, "mfma_bf16_256x128x32_w2x2_s3", 2},
-    {128, 256, 32, 256, 4, "mfma_bf16_128x256x32_w2x2_s3", 2},
-    {128, 128, 64, 256, 6, "mfma_bf16_128x128x64_w2x2_s3", 1},
-    {256, 128, 64, 256, 7, "mfma_bf16_256x128x64_w2x2_s3", 1},
-    {128, 256, 32, 256, 8, "mfma_bf16_128x256x32_w2x2_s2", 2},
-    {128, 128, 32, 256, 9, "mfma_bf16_128x128x32_w2x2_s2", 4},
+    DG_TILE16(bf16, 256, 256, 64, 2, 5),
+    DG_TILE16(bf16, 128, 128, 32, 4, 1),
+    DG_TILE16(bf16, 256, 256, 32, 4, 0),
+    DG_TILE16(bf16, 256, 128, 32, 4, 2),
+    DG_TILE16(bf16, 256, 128, 32, 3, 3),
+    DG_TILE16(bf16, 128, 256, 32, 3, 4),
+    DG_TILE16(bf16, 128, 128, 64, 3, 6),
+    DG_TILE16(bf16, 256, 128, 64, 3, 7),
+    DG_TILE16(bf16, 128, 256, 32, 2, 8),
+    DG_TILE16(bf16, 128, 128, 32, 2, 9),
 };
 const int kNumMfmaBf16Tiles = 10;
 
 const TileConfig kMfmaF16Tiles[] = {
-    {256, 256, 64, 256, 5, "mfma_f16_256x256x64_w2x2_s2", 1},
-    {128, 128, 32, 256, 1, "mfma_f16_128x128x32_w2x2_s4", 2},
+    DG_TILE16(f16, 256, 256, 64, 2, 5),
+    DG_TILE16(f16, 128, 128, 32, 4, 1),
 };
+#undef DG_TILE16
 const int kNumMfmaF16Tiles = 2;
 
 hipError_t launch_mfma16(const GemmArgs &g, const Plan &p, hipStream_t stream)

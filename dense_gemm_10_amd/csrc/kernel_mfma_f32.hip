@@ -272,7 +272,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f32_kernel(GemmArgs g)
     }
 
     // the launch gives the kernel max(loop buffers, epilogue) bytes of LDS
-    tile_epilogue<BM, BN, WM, WN>(g, tc, smem, m0, n0, acc);
+    // 256 x 256 tiles run one workgroup per CU (512 registers per lane),
+    // 128 x 128 tiles two
+    tile_epilogue<BM, BN, WM, WN, (BM * BN >= 256 * 256 ? 512 : 256)>(g, tc, smem, m0, n0, acc);
 }
 
 template <int BM, int BN, int WM, int WN, int FBK>
