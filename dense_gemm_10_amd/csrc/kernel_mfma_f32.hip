@@ -252,7 +252,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_f32_kernel(GemmArgs g)
             load_tiles_masked(kb);
         }
         store_tiles(0);
-        for (int64_t kt = 0; kt < nk; ++kt) {
+        int64_t kt = 0;
+        // Steady state of an interior tile: the next K tile is whole, its
+        // loads are unmasked and spread over this tile's body.  With the
+        // flags constant the body has no branches, and the compiler counts
+        // outstanding loads exactly; behind runtime flags it waited for all
+        // of them (vmcnt(0)) in the middle of the matrix work.
+        if (interior) {
+            for (; kt + 1 < nk_full; ++kt) {
+                lds_barrier();
+                tile_body((int)(kt & 1), true, kb + (kt + 1) * FBK, false);
+            }
+        }
+        for (; kt < nk; ++kt) {
             const int st = (int)(kt & 1);
             const bool has_next = kt + 1 < nk;
             const bool fast_next = has_next && interior && kt + 1 < nk_full;
