@@ -147,6 +147,26 @@ def _csv_rows(outdir, suffix):
         return list(csv.DictReader(f))
 
 
+# Default timed calls and warmup.  The clock settles over the first ~20 ms
+# of a fresh run (the fp32 4096^3 call falls from ~1.27 ms to ~1.07 ms over
+# its first 20 calls), so the default warmup covers that before the timed
+# calls; the kernel-trace pass of --collect-profile runs the same counts.
+DEFAULT_STEPS = 50
+DEFAULT_WARMUP = 30
+
+
+def _timed_means(out, warmup):
+    """Mean duration (ns) per kernel over its dispatches after the first
+    `warmup` (the bench's timed calls), from a --kernel-trace CSV."""
+    import collections
+    rows = sorted(_csv_rows(out, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    per = collections.defaultdict(list)
+    for r in rows:
+        per[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return [{"Name": k, "Calls": len(v) - warmup, "AverageNs": sum(v[warmup:]) / (len(v) - warmup)}
+            for k, v in per.items() if len(v) > warmup]
+
+
 def _per_dispatch(rows, name_filter):
     """Mean over dispatches of the per-dispatch sum (over instances) of the
     counter, for kernels whose name contains name_filter."""
@@ -181,13 +201,15 @@ def collect_profile(workload, tmp, out_dir=PROFILES, knobs=()):
     results = {}
     # 1. kernel trace with statistics
     out = os.path.join(tmp, "trace")
-    cmd = _rocprof(["--kernel-trace", "--stats"], out) + child + ["--steps", "20", "--warmup", "5"]
+    cmd = _rocprof(["--kernel-trace", "--stats"], out) + child + [
+        "--steps", str(DEFAULT_STEPS), "--warmup", str(DEFAULT_WARMUP)]
     log(f"[profile] {' '.join(cmd)}")
     subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL)
     stats = _csv_rows(out, "kernel_stats.csv")
     results["trace_command"] = _shown(cmd, tmp)
     results["kernel_stats"] = [{k: r[k] for k in ("Name", "Calls", "AverageNs", "MinNs", "MaxNs",
                                                  "Percentage")} for r in stats]
+    results["timed_means"] = _timed_means(out, DEFAULT_WARMUP)
     # 2. traffic counters, GEMM and copy calibration
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         out = os.path.join(tmp, counter)
@@ -261,6 +283,13 @@ def write_profile(results, out_dir=PROFILES):
         lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
                      f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | "
                      f"{float(r['Percentage']):.2f} |")
+    if results.get("timed_means"):
+        lines += ["", "The statistics above cover every dispatch, warmup included. Over the "
+                  "timed calls only (the dispatches after each kernel's first "
+                  f"{DEFAULT_WARMUP}), the same trace gives:", "",
+                  "| kernel | timed calls | average ns |", "|---|---|---|"]
+        for r in results["timed_means"]:
+            lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {r['AverageNs']:.0f} |")
     lines += ["", "## HBM traffic per GEMM dispatch", "",
               "| counter | KiB / dispatch | copy calibration KiB (512 MiB copy) | scale | bytes |",
               "|---|---|---|---|---|"]
@@ -332,11 +361,8 @@ def cpu_baseline(name, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # The clock settles over the first ~20 ms of a fresh run (the fp32 4096^3
-    # call falls from ~1.27 ms to ~1.07 ms over its first 20 calls), so the
-    # default warmup covers that before the timed steps.
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=DEFAULT_STEPS)
+    ap.add_argument("--warmup", type=int, default=DEFAULT_WARMUP)
     import workloads as W
     ap.add_argument("--workload", default="c2", choices=list(W.WORKLOADS) + ["copy"])
     ap.add_argument("--secondary", default="c3",
