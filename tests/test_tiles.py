@@ -21,18 +21,27 @@ def _need_gpu():
 
 
 def _problem(family, epilogue):
+    """`epilogue`: "plain" (alpha 1, beta 0); "ragged" (alpha, beta * C, bias
+    and GELU with N = 387, so no output row starts on a 16-byte boundary:
+    the general row path); "aligned" and "aligned_gelu" (the same terms
+    with N = 392 and the family's own output type: interior tiles take the
+    whole-tile path, edge tiles the general one)."""
     dt = {"mfma_bf16": W.BF16, "mfma_f16": W.F16, "mfma_f32": W.F32}[family]
     if dt == W.F32:
         base = dict(M=520, N=392, K=300, a_type=dt, b_type=dt, c_type=W.F32)
     else:
         base = dict(M=520, N=392, K=1000, a_type=dt, b_type=dt, a_order=W.ROW, b_order=W.COL,
                     c_type=dt)
-    if epilogue:
-        base.update(c_type=W.F32, alpha=1.5, beta=0.5, has_bias=True, bias_type=dt,
-                    act=W.ACT_GELU_ERF, N=392 - 5)
+    terms = dict(alpha=1.5, beta=0.5, has_bias=True, bias_type=dt)
+    if epilogue == "ragged":
+        base.update(terms, c_type=W.F32, act=W.ACT_GELU_ERF, N=392 - 5)
         if dt == W.F32:
             base.update(ldb=392)     # row-major B: the fp32 kernels need ldb % 4 == 0
-    return W.Problem(name=f"{family}_{'epi' if epilogue else 'plain'}", seed=61, **base)
+    elif epilogue == "aligned":
+        base.update(terms)
+    elif epilogue == "aligned_gelu":
+        base.update(terms, act=W.ACT_GELU_TANH)
+    return W.Problem(name=f"{family}_{epilogue}", seed=61, **base)
 
 
 CASES = [(f, t, s) for f, tiles in TILES.items() for t in tiles for s in (1, 2)]
@@ -40,7 +49,7 @@ CASES = [(f, t, s) for f, tiles in TILES.items() for t in tiles for s in (1, 2)]
 
 @pytest.mark.parametrize("family,tile,schedule", CASES,
                          ids=[f"{t}-{'dp' if s == 1 else 'sk'}" for _, t, s in CASES])
-@pytest.mark.parametrize("epilogue", [False, True])
+@pytest.mark.parametrize("epilogue", ["plain", "ragged", "aligned", "aligned_gelu"])
 def test_every_tile(family, tile, schedule, epilogue, monkeypatch):
     from workloads.device import DeviceProblem
     monkeypatch.setenv("DG_FORCE_TILE", tile)
