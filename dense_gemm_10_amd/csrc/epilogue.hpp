@@ -177,21 +177,28 @@ __device__ __forceinline__ void static_for(F &&f)
     }
 }
 
-// Epilogue of a whole tile (all BM x BN outputs inside the output) whose
-// rows all start on a 16-byte boundary: the common interior case of
-// tile_epilogue_rows, with its arithmetic and stores, minus the per-run
-// alignment and edge logic.  Chunk c holds block row c of every wave's
+// Epilogue of a whole tile (all BM x BN outputs inside the output): the
+// interior case of tile_epilogue_rows, with its arithmetic and stores, minus
+// the per-run bounds logic.  Chunk c holds block row c of every wave's
 // accumulators (32 * WM tile rows, so all waves stage each chunk).  Thread
-// t owns one 16-byte column run, the same in every row it stores, and the
-// rows t / RPR + q * (NT / RPR) of each chunk.  The runs are taken in
-// groups whose values fit the registers left beside the accumulators (REGS
-// per lane in all, the budget the kernel was compiled to): all of a group's
-// LDS reads (and C reads when beta != 0) are issued before its first
-// store, so their latencies overlap instead of adding up run after run.
-template <int BM, int BN, int WM, int WN, bool PARTIAL, int OUT, int REGS>
-__device__ __forceinline__ void tile_epilogue_aligned(const GemmArgs &g, char *out, int64_t ld,
-                                                      int64_t n0, float *lds,
-                                                      const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
+// t owns one column slot js = t mod RPR and the rows t / RPR + q * (NT / RPR)
+// of each chunk.  The runs are taken in groups whose values fit the
+// registers left beside the accumulators (REGS per lane in all, the budget
+// the kernel was compiled to): all of a group's LDS reads (and C reads when
+// beta != 0) are issued before its first store, so their latencies overlap
+// instead of adding up run after run.
+//
+// Without SHIFTED every row starts on a 16-byte boundary and slot js is the
+// row's 16-byte block js.  With SHIFTED, row r starts s(r) = (d0 + r * dl)
+// mod VEC elements past a boundary and is staged shifted right by s(r), so
+// each 16-byte block of the output row is one aligned vector of the staged
+// row.  A row with s > 0 has a partial head block, RPR - 1 full blocks and
+// a partial tail block: slot js takes full block js + 1 (the last slot has
+// none), and a pass per chunk stores the head and tail elements one by one.
+template <int BM, int BN, int WM, int WN, bool PARTIAL, int OUT, int REGS, bool SHIFTED>
+__device__ __forceinline__ void tile_epilogue_whole(const GemmArgs &g, char *out, int64_t ld,
+                                                    int64_t n0, float *lds, int d0, int dl,
+                                                    const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
 {
     constexpr int NT = 64 * WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -199,13 +206,16 @@ __device__ __forceinline__ void tile_epilogue_aligned(const GemmArgs &g, char *o
     constexpr int CH_ROWS = 32 * WM;                  // tile rows per chunk
     constexpr int EP_LD = epilogue_ld(BN);
     constexpr bool HALF_OUT = OUT != DT_F32;
-    constexpr int VEC = HALF_OUT ? 8 : 4;             // outputs per 16-byte run
+    constexpr int VEC = HALF_OUT ? 8 : 4;             // outputs per 16-byte block
     constexpr int ES = HALF_OUT ? 2 : 4;              // output element size
-    constexpr int RPR = BN / VEC;                     // runs per row
+    constexpr int RPR = BN / VEC;                     // column slots (full blocks of an aligned row)
     constexpr int RSTEP = NT / RPR;                   // chunk rows between a thread's runs
     constexpr int RUNS = CH_ROWS / RSTEP;             // runs per thread per chunk
+    constexpr int EDGE = CH_ROWS * 2 * VEC / NT;      // head / tail elements per thread per chunk
     static_assert(CH_ROWS <= kEpilogueRows, "chunk fits the staging buffer");
     static_assert(NT % RPR == 0 && 32 % RSTEP == 0 && RUNS * RSTEP == CH_ROWS, "run split");
+    static_assert(EDGE * NT == CH_ROWS * 2 * VEC, "edge split");
+    static_assert(epilogue_ld(BN) >= BN + VEC, "room for the row shift and the tail block");
     // registers per run in flight (values, and C's when beta != 0); about
     // 40 more stay with addresses, bias and loop state
     constexpr int PER_RUN = VEC + (PARTIAL ? 0 : 4);
@@ -217,29 +227,53 @@ __device__ __forceinline__ void tile_epilogue_aligned(const GemmArgs &g, char *o
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int frag_half = lane >> 5;
-    const int col = (tid % RPR) * VEC;                // tile column of the thread's run
+    const int js = tid % RPR;                         // column slot
     const int rt = tid / RPR;                         // first chunk row of the thread
     const int64_t ld_bytes = ld * ES;
-    char *base = out + (int64_t)rt * ld_bytes + (int64_t)col * ES;
-    const float *rd = lds + rt * EP_LD + col;
+    char *rowbase = out + (int64_t)rt * ld_bytes;
+    const float *rdrow = lds + rt * EP_LD;
+    float *bias_s = lds + kEpilogueRows * EP_LD;      // SHIFTED: the tile's bias
+    // misalignment (elements) of tile row r
+    auto shift = [&](int r) { return SHIFTED ? (d0 + r * dl) & (VEC - 1) : 0; };
+    // chunk row cr of chunk c is tile row (cr / 32) * TM + c * 32 + cr % 32
+    auto tile_row = [&](int c, int cr) { return (cr / 32) * TM + c * 32 + cr % 32; };
     float bias[VEC];
     const bool has_bias = !PARTIAL && g.bias;
     if (has_bias) {
+        if (SHIFTED) {
+            for (int t = tid; t < BN; t += NT)
+                bias_s[t] = load_as_f32(g.bias, g.bias_type, n0 + t);
+        } else {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            bias[e] = load_as_f32(g.bias, g.bias_type, n0 + col + e);
+            for (int e = 0; e < VEC; ++e)
+                bias[e] = load_as_f32(g.bias, g.bias_type, n0 + js * VEC + e);
+        }
     }
     const bool read_c = !PARTIAL && g.beta != 0.0f;
-    // Block row I of the wave's accumulators -> chunk rows wm * 32 + [0, 32).
+    // Block row I of the wave's accumulators -> chunk rows wm * 32 + [0, 32),
+    // each shifted by its tile row's misalignment.
     auto stage = [&](auto I) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int row = wm * 32 + 8 * (v / 4) + 4 * frag_half + (v % 4);
-            float *dst = lds + row * EP_LD + wn * TN + (lane & 31);
+            const int rb = 8 * (v / 4) + 4 * frag_half + (v % 4);
+            float *dst = lds + (wm * 32 + rb) * EP_LD + shift(wm * TM + decltype(I)::value * 32 + rb) +
+                         wn * TN + (lane & 31);
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 dst[j * 32] = acc[decltype(I)::value][j][v];
         }
+    };
+    // alpha, beta * C, bias and activation of one value at tile column col
+    // (the edge elements; the runs apply the same steps group-wide).
+    auto finish_one = [&](float v, const char *cptr, int col) {
+        if (PARTIAL)
+            return v;
+        v *= g.alpha;
+        if (read_c)
+            v = fmaf(g.beta, HALF_OUT ? half_to_f32<OUT>(*(const uint16_t *)cptr) : *(const float *)cptr, v);
+        if (has_bias)
+            v += bias_s[col];
+        return activate(v, g.act);
     };
     // One copy of the chunk code per chunk, each with its chunk index a
     // constant: a loop over the chunks, unrolled or not, leaves the
@@ -249,24 +283,35 @@ __device__ __forceinline__ void tile_epilogue_aligned(const GemmArgs &g, char *o
         constexpr int c = decltype(I)::value;
         stage(I);
         lds_barrier();
-        // chunk row rt + q * RSTEP is tile row (q * RSTEP / 32) * TM + c * 32 + (q * RSTEP) % 32 + rt
         static_for<RUNS / GROUP>([&](auto G) {
             constexpr int q0 = decltype(G)::value * GROUP;
+            // run u: chunk row rt + q * RSTEP, tile row trow[u] (relative to
+            // row rt), 16-byte block at tile column col[u]; full[u] is false
+            // for the last slot of a shifted row, which has no full block
+            int trow[GROUP], blk[GROUP], col[GROUP];
+            bool full[GROUP];
+#pragma unroll
+            for (int u = 0; u < GROUP; ++u) {
+                const int q = q0 + u;
+                trow[u] = tile_row(c, q * RSTEP);
+                const int sh = shift(trow[u] + rt);
+                blk[u] = js + (sh != 0 ? 1 : 0);
+                col[u] = blk[u] * VEC - sh;
+                full[u] = !SHIFTED || sh == 0 || js < RPR - 1;
+            }
             uint4 cin[GROUP];
             if (read_c) {
 #pragma unroll
-                for (int u = 0; u < GROUP; ++u) {
-                    const int q = q0 + u;
-                    const int trow = (q * RSTEP / 32) * TM + c * 32 + (q * RSTEP) % 32;
-                    cin[u] = *(const uint4 *)(base + (int64_t)trow * ld_bytes);
-                }
+                for (int u = 0; u < GROUP; ++u)
+                    if (full[u])
+                        cin[u] = *(const uint4 *)(rowbase + (int64_t)trow[u] * ld_bytes + (int64_t)col[u] * ES);
             }
             float v[GROUP][VEC];
 #pragma unroll
             for (int u = 0; u < GROUP; ++u)
 #pragma unroll
                 for (int e = 0; e < VEC; e += 4) {
-                    const float4 x = *(const float4 *)&rd[(q0 + u) * RSTEP * EP_LD + e];
+                    const float4 x = *(const float4 *)&rdrow[(q0 + u) * RSTEP * EP_LD + blk[u] * VEC + e];
                     v[u][e] = x.x; v[u][e + 1] = x.y; v[u][e + 2] = x.z; v[u][e + 3] = x.w;
                 }
             // Each step covers the whole group, so every uniform branch
@@ -293,8 +338,14 @@ __device__ __forceinline__ void tile_epilogue_aligned(const GemmArgs &g, char *o
 #pragma unroll
                     for (int u = 0; u < GROUP; ++u)
 #pragma unroll
-                        for (int e = 0; e < VEC; ++e)
-                            v[u][e] += bias[e];
+                        for (int e = 0; e < VEC; ++e) {
+                            if (SHIFTED) {
+                                const int bc = col[u] + e;   // past BN only in a slot without a block
+                                v[u][e] += bias_s[bc < BN ? bc : BN - 1];
+                            } else {
+                                v[u][e] += bias[e];
+                            }
+                        }
                 }
                 auto act_all = [&](auto A) {
 #pragma unroll
@@ -310,9 +361,9 @@ __device__ __forceinline__ void tile_epilogue_aligned(const GemmArgs &g, char *o
             }
 #pragma unroll
             for (int u = 0; u < GROUP; ++u) {
-                const int q = q0 + u;
-                const int trow = (q * RSTEP / 32) * TM + c * 32 + (q * RSTEP) % 32;
-                char *dst = base + (int64_t)trow * ld_bytes;
+                if (!full[u])
+                    continue;
+                char *dst = rowbase + (int64_t)trow[u] * ld_bytes + (int64_t)col[u] * ES;
                 if (HALF_OUT) {
                     uint32_t w[4];
 #pragma unroll
@@ -325,6 +376,29 @@ __device__ __forceinline__ void tile_epilogue_aligned(const GemmArgs &g, char *o
                 }
             }
         });
+        if constexpr (SHIFTED) {
+            // head block (elements s .. VEC-1 at tile columns 0 .. VEC-s-1)
+            // and tail block (elements 0 .. s-1 at tile columns BN-s .. BN-1)
+            // of every shifted chunk row, EDGE elements per thread
+#pragma unroll
+            for (int i = 0; i < EDGE; ++i) {
+                const int slot = tid * EDGE + i;
+                const int cr = slot / (2 * VEC), k = slot % (2 * VEC);
+                const int tr = tile_row(c, cr);
+                const int sh = shift(tr);
+                const bool head = k < VEC;
+                const int e = head ? k : k - VEC;
+                if (sh == 0 || (head ? e < sh : e >= sh))
+                    continue;
+                const int tc = head ? e - sh : BN - sh + e;
+                char *dst = out + (int64_t)tr * ld_bytes + (int64_t)tc * ES;
+                const float v = finish_one(lds[cr * EP_LD + (head ? 0 : BN) + e], dst, tc);
+                if (HALF_OUT)
+                    *(uint16_t *)dst = f32_to_half<OUT>(v);
+                else
+                    *(float *)dst = v;
+            }
+        }
         lds_barrier();
     });
 }
@@ -363,8 +437,11 @@ __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out,
     const int d0 = (int)(((uintptr_t)out % 16) / ES);
     const int dl = (int)(ld % VEC);
     auto shift = [&](int r) { return (d0 + r * dl) & (VEC - 1); };
-    if (rows == BM && cols == BN && d0 == 0 && dl == 0) {
-        tile_epilogue_aligned<BM, BN, WM, WN, PARTIAL, OUT, REGS>(g, out, ld, n0, lds, acc);
+    if (rows == BM && cols == BN) {
+        if (d0 == 0 && dl == 0)
+            tile_epilogue_whole<BM, BN, WM, WN, PARTIAL, OUT, REGS, false>(g, out, ld, n0, lds, 0, 0, acc);
+        else
+            tile_epilogue_whole<BM, BN, WM, WN, PARTIAL, OUT, REGS, true>(g, out, ld, n0, lds, d0, dl, acc);
         return;
     }
     const bool has_bias = !PARTIAL && g.bias;
