@@ -110,6 +110,52 @@ __global__ __launch_bounds__(GTHREADS) void gemm_generic_kernel(GemmArgs g)
     }
 }
 
+// p[0] + p[stride] + ... + p[(count - 1) * stride], added left to right (a
+// fixed order, so the result is reproducible), with the loads of up to
+// eight partials issued before their additions: a loop of dependent
+// load-add pairs waits one memory latency per partial.
+template <typename V>
+__device__ __forceinline__ void add_to(V &sum, const V &v);
+template <>
+__device__ __forceinline__ void add_to<float>(float &sum, const float &v) { sum += v; }
+template <>
+__device__ __forceinline__ void add_to<float4>(float4 &sum, const float4 &v)
+{
+    sum.x += v.x;
+    sum.y += v.y;
+    sum.z += v.z;
+    sum.w += v.w;
+}
+
+template <typename V>
+__device__ __forceinline__ V sum_partials(const float *p, int64_t stride, int64_t count)
+{
+    V sum{};
+    int64_t s = 0;
+    for (; s + 8 <= count; s += 8) {
+        V v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            v[j] = *(const V *)(p + (s + j) * stride);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            add_to(sum, v[j]);
+    }
+    if (s + 4 <= count) {
+        V v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = *(const V *)(p + (s + j) * stride);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            add_to(sum, v[j]);
+        s += 4;
+    }
+    for (; s < count; ++s)
+        add_to(sum, *(const V *)(p + s * stride));
+    return sum;
+}
+
 // Split-K reduction: for each output element, sum the S partials in split
 // order (a fixed order, so the result is reproducible), then apply the
 // epilogue exactly once.
@@ -119,9 +165,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int32_t 
     const int64_t plane = total;                  // one split's partials
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
          e += (int64_t)gridDim.x * 256) {
-        float sum = 0.0f;
-        for (int32_t s = 0; s < splits; ++s)
-            sum += g.ws[(int64_t)s * plane + e];
+        const float sum = sum_partials<float>(g.ws + e, plane, splits);
         const int64_t n = e % g.N;
         const int64_t bm = e / g.N;
         const int64_t m = bm % g.M;
@@ -139,14 +183,7 @@ __global__ __launch_bounds__(256) void splitk_reduce4_kernel(GemmArgs g, int32_t
     const uint32_t N = (uint32_t)g.N, M = (uint32_t)g.M;
     for (uint32_t e = (blockIdx.x * 256u + threadIdx.x) * 4u; e < total;
          e += gridDim.x * 1024u) {
-        float4 sum = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        for (int32_t s = 0; s < splits; ++s) {
-            const float4 v = *(const float4 *)(g.ws + (int64_t)s * total + e);
-            sum.x += v.x;
-            sum.y += v.y;
-            sum.z += v.z;
-            sum.w += v.w;
-        }
+        const float4 sum = sum_partials<float4>(g.ws + e, total, splits);
         const uint32_t row = e / N, n = e - row * N;
         const uint32_t b = row / M, m = row - b * M;
         const float acc[4] = {sum.x, sum.y, sum.z, sum.w};
@@ -172,14 +209,8 @@ __global__ __launch_bounds__(256) void streamk_fixup_kernel(GemmArgs g, int32_t 
     if (m >= g.M)
         return;
     const float *p = g.sk_parts + r * g.sk.tail_splits * area + e0;
-    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t s = 0; s < g.sk.tail_splits; ++s) {
-        const float4 v = *(const float4 *)(p + s * area);
-        sum[0] += v.x;
-        sum[1] += v.y;
-        sum[2] += v.z;
-        sum[3] += v.w;
-    }
+    const float4 t = sum_partials<float4>(p, area, g.sk.tail_splits);
+    const float sum[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t n = n0 + col + j;
