@@ -39,6 +39,7 @@ SOURCES = [
     "kernel_valu_f32.hip",
     "kernel_mfma16.hip",
     "kernel_mfma_f32.hip",
+    "kernel_sliver.hip",
 ]
 
 

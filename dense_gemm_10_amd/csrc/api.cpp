@@ -248,6 +248,31 @@ const TileConfig *tile_named(const TileConfig *table, int n, const char *name)
     return nullptr;
 }
 
+// DG_FORCE_PLAN=<tile>:<dp|sk>:<splits> (the offline tuning sweep): an
+// entry for any problem on the tile's family, applied exactly as a tuned
+// entry is.  False when unset or when the tile is not in `table`.
+bool forced_plan(const TileConfig *table, int n, Kernel k, TunedEntry *out)
+{
+    static char name[96];
+    const char *env = getenv("DG_FORCE_PLAN");
+    if (!env)
+        return false;
+    const char *c1 = strchr(env, ':');
+    const char *c2 = c1 ? strchr(c1 + 1, ':') : nullptr;
+    if (!c1 || !c2 || c1 - env >= (ptrdiff_t)sizeof name)
+        return false;
+    memcpy(name, env, c1 - env);
+    name[c1 - env] = 0;
+    if (!tile_named(table, n, name))
+        return false;
+    memset(out, 0, sizeof *out);
+    out->kernel = k;
+    out->tile = name;
+    out->schedule = strncmp(c1 + 1, "sk", 2) == 0 ? DG_SCHED_STREAM_K : DG_SCHED_DATA_PARALLEL;
+    out->splits = atoi(c2 + 1);
+    return true;
+}
+
 // The tuned entry for this problem on kernel family k whose tile exists in
 // `table`, or NULL.
 const TunedEntry *find_tuned(const dg_gemm_desc *d, Kernel k, const TileConfig *table, int n)
@@ -410,8 +435,12 @@ dg_status finish_plan(const dg_gemm_desc *d, Plan p, size_t ws_avail, bool ws_kn
 }
 
 
+// `key`: the problem to look up in the tuned table (default d).  `keep`:
+// without a tuned or forced entry, plan on this tile of the family instead
+// of choosing one.
 dg_status make_plan(const dg_gemm_desc *d, const void *A, const void *B, size_t ws_avail,
-                    bool ws_known, Plan *plan)
+                    bool ws_known, Plan *plan, const dg_gemm_desc *key = nullptr,
+                    const TileConfig *keep = nullptr)
 {
     Plan p{};
     const int32_t algo = d->algo;
@@ -457,12 +486,19 @@ dg_status make_plan(const dg_gemm_desc *d, const void *A, const void *B, size_t 
     // its better flop-per-byte ratio wins: 4352 x 4352 x 8192 (bf16) ran
     // 295 us that way against 415 us on 128 x 128 tiles.
     const TunedEntry *tuned = nullptr;
-    if (table && !forced_tile(table, ntab))
-        tuned = find_tuned(d, p.kernel, table, ntab);
+    TunedEntry forced;
+    if (table && forced_plan(table, ntab, p.kernel, &forced))
+        tuned = &forced;
+    else if (table && !forced_tile(table, ntab))
+        tuned = find_tuned(key ? key : d, p.kernel, table, ntab);
     if (tuned) {
         p.tile = *tile_named(table, ntab, tuned->tile);
         p.tuned = 1;
         return finish_plan(d, p, ws_avail, ws_known, tuned->schedule, tuned->splits, plan);
+    }
+    if (table && keep) {
+        p.tile = *keep;
+        return finish_plan(d, p, ws_avail, ws_known, 0, 0, plan);
     }
     if (table16 && !forced_tile(table16, n16) && p.tile.bm != table16[0].bm) {
         Plan big = p;
@@ -475,6 +511,61 @@ dg_status make_plan(const dg_gemm_desc *d, const void *A, const void *B, size_t 
         }
     }
     return finish_plan(d, p, ws_avail, ws_known, 0, 0, plan);
+}
+
+// A whole call: the plan of the tiled kernel over columns [0, main.N) and,
+// when nrem > 0, the sliver kernel over the last nrem columns.
+struct CallPlan {
+    dg_gemm_desc main;      // the caller's problem with N cut to the full tile columns
+    Plan plan;              // plan of `main`
+    int32_t nrem;           // sliver columns (0: none)
+};
+
+// The tiled kernels spend a whole tile column on the few columns past the
+// last full one and leave their last wave nearly empty: 4095 x 4097 x 1000
+// on 128 x 256 tiles is 544 tiles for 512 resident workgroups, and the 32
+// tiles of its last column hold one valid column each.  When the library
+// chooses the schedule (no split-K or schedule asked for), the plan's tile
+// leaves 1 .. kMaxSliver columns past the last full tile column, the full
+// columns alone make at least one tile per compute unit, and A is
+// row-major with 16-byte aligned rows, the call runs the tiled plan on the
+// full columns and the sliver kernel on the rest.  The full columns' plan
+// is looked up in the tuned table under the caller's shape; without an
+// entry it keeps the whole grid's tile (re-choosing one for the narrower
+// grid took 256 x 256 tiles on the GELU problem: 95 us, against 80 us on
+// the 128 x 128 tiles the whole grid chose and 92 us without the split).
+// A tuned plan that puts a stream-K tail on the whole grid (the sweep
+// timed it against the split) is kept as it is.
+dg_status make_call_plan(const dg_gemm_desc *d, const void *A, const void *B, size_t ws_avail,
+                         bool ws_known, CallPlan *cp)
+{
+    cp->main = *d;
+    cp->nrem = 0;
+    dg_status st = make_plan(d, A, B, ws_avail, ws_known, &cp->plan);
+    if (st != DG_SUCCESS)
+        return st;
+    const Plan &p = cp->plan;
+    const bool tiled = p.kernel == KERNEL_MFMA_BF16 || p.kernel == KERNEL_MFMA_F16 ||
+                       p.kernel == KERNEL_MFMA_F32;
+    if (!tiled || (p.tuned && p.sk.tail_tiles > 0) || d->algo != DG_ALGO_AUTO ||
+        d->schedule != DG_SCHED_AUTO || d->split_k != 0 ||
+        !reads_ab(d) || d->a_order != DG_ROW_MAJOR ||
+        (d->lda * elem_size(d->a_type)) % 16 != 0 || (A && !aligned_to(A, 16)))
+        return DG_SUCCESS;
+    const int64_t nrem = d->N % p.tile.bn;
+    const int64_t n_main = d->N - nrem;
+    if (nrem == 0 || nrem > kMaxSliver || n_main < p.tile.bn ||
+        ceil_div(d->M, p.tile.bm) * (n_main / p.tile.bn) * d->batch < kNumCu)
+        return DG_SUCCESS;
+    dg_gemm_desc m = *d;
+    m.N = n_main;
+    Plan pm;
+    if (make_plan(&m, A, B, ws_avail, ws_known, &pm, d, p.tuned ? nullptr : &p.tile) != DG_SUCCESS)
+        return DG_SUCCESS;           // keep the single plan
+    cp->main = m;
+    cp->plan = pm;
+    cp->nrem = (int32_t)nrem;
+    return DG_SUCCESS;
 }
 
 void fill_args(const dg_gemm_desc *d, const Plan &p, const void *A, const void *B, void *C,
@@ -557,11 +648,11 @@ dg_status dg_gemm_workspace_size(const dg_gemm_desc *d, size_t *bytes)
     *bytes = 0;
     if (is_noop(d))
         return DG_SUCCESS;
-    Plan p;
-    st = make_plan(d, nullptr, nullptr, 0, false, &p);
+    CallPlan cp;
+    st = make_call_plan(d, nullptr, nullptr, 0, false, &cp);
     if (st != DG_SUCCESS)
         return st;
-    *bytes = p.workspace_bytes;
+    *bytes = cp.plan.workspace_bytes;
     return DG_SUCCESS;
 }
 
@@ -577,10 +668,11 @@ dg_status dg_gemm_describe(const dg_gemm_desc *d, size_t workspace_bytes, char *
         snprintf(buf, len, "noop");
         return DG_SUCCESS;
     }
-    Plan p;
-    st = make_plan(d, nullptr, nullptr, workspace_bytes, true, &p);
+    CallPlan cp;
+    st = make_call_plan(d, nullptr, nullptr, workspace_bytes, true, &cp);
     if (st != DG_SUCCESS)
         return st;
+    const Plan &p = cp.plan;
     char sched[128];
     if (p.sk.tail_tiles > 0)
         snprintf(sched, sizeof sched,
@@ -592,12 +684,12 @@ dg_status dg_gemm_describe(const dg_gemm_desc *d, size_t workspace_bytes, char *
     snprintf(buf, len,
              "kernel=%s tile=%s bm=%d bn=%d bk=%d threads=%d splits=%d k_per_split=%lld "
              "programs=%lld group_m=%d xcd_remap=%d workspace=%zu reduce_blocks=%lld "
-             "fixup_blocks=%lld tuned=%d schedule=%s",
+             "fixup_blocks=%lld tuned=%d schedule=%s sliver=%d",
              kernel_name(p.kernel), p.tile.name, p.tile.bm, p.tile.bn, p.tile.bk, p.tile.threads,
              p.splits, (long long)p.k_per_split, (long long)p.programs,
              d->group_m > 0 ? d->group_m : kDefaultGroupM, d->xcd_remap >= 0 ? 1 : 0,
              p.workspace_bytes, (long long)p.reduce_blocks, (long long)p.fixup_blocks, p.tuned,
-             sched);
+             sched, cp.nrem);
     return DG_SUCCESS;
 }
 
@@ -613,10 +705,11 @@ dg_status dg_gemm(const dg_gemm_desc *d, const void *A, const void *B, void *C, 
         return st;
     if (is_noop(d))
         return DG_SUCCESS;
-    Plan p;
-    st = make_plan(d, A, B, workspace ? workspace_bytes : 0, true, &p);
+    CallPlan cp;
+    st = make_call_plan(d, A, B, workspace ? workspace_bytes : 0, true, &cp);
     if (st != DG_SUCCESS)
         return st;
+    const Plan &p = cp.plan;
     if (p.workspace_bytes > 0) {
         if (!workspace || workspace_bytes < p.workspace_bytes)
             return DG_ERROR_INSUFFICIENT_WORKSPACE;
@@ -625,7 +718,7 @@ dg_status dg_gemm(const dg_gemm_desc *d, const void *A, const void *B, void *C, 
             return DG_ERROR_INVALID_VALUE;
     }
     GemmArgs g;
-    fill_args(d, p, A, B, C, workspace, &g);
+    fill_args(&cp.main, p, A, B, C, workspace, &g);
     hipStream_t s = (hipStream_t)stream;
     hipError_t err = hipSuccess;
     switch (p.kernel) {
@@ -645,6 +738,13 @@ dg_status dg_gemm(const dg_gemm_desc *d, const void *A, const void *B, void *C, 
     }
     if (p.sk.tail_tiles > 0) {
         err = launch_streamk_fixup(g, p, s);
+        if (err != hipSuccess)
+            return DG_ERROR_LAUNCH;
+    }
+    if (cp.nrem > 0) {
+        GemmArgs gs;
+        fill_args(d, p, A, B, C, nullptr, &gs);
+        err = launch_sliver(gs, cp.main.N, cp.nrem, s);
         if (err != hipSuccess)
             return DG_ERROR_LAUNCH;
     }

@@ -91,18 +91,22 @@ class Timer:
         self.fields = W.desc_fields(p)
         self.fields["bias"] = self.dp.bias.data_ptr() if self.dp.bias is not None else None
 
-    def plan(self, tile=None, schedule=0, tuned=False, split_k=None):
-        """(description, desc) of the plan with DG_FORCE_TILE = tile."""
+    def plan(self, tile=None, schedule=0, split_k=None):
+        """(description, desc, workspace bytes) of a candidate.  With a tile,
+        the plan a table entry (tile, schedule 1 = data-parallel or 2 =
+        stream-K, split_k slices, None = automatic) gives, applied through
+        DG_FORCE_PLAN exactly as the planner applies a tuned entry (the
+        descriptor leaves schedule and split to the library, so the
+        sliver-column split applies as it will at run time); without, the
+        heuristic plan (DG_TUNED=0)."""
         import dense_gemm_10_amd as dg
-        os.environ["DG_TUNED"] = "1" if tuned else "0"
+        os.environ["DG_TUNED"] = "0"
+        os.environ.pop("DG_FORCE_TILE", None)
         if tile:
-            os.environ["DG_FORCE_TILE"] = tile
+            os.environ["DG_FORCE_PLAN"] = f"{tile}:{'sk' if schedule == 2 else 'dp'}:{split_k or 0}"
         else:
-            os.environ.pop("DG_FORCE_TILE", None)
-        f = dict(self.fields, schedule=schedule)
-        if split_k is not None:
-            f["split_k"] = split_k
-        d = dg.make_desc(**f)
+            os.environ.pop("DG_FORCE_PLAN", None)
+        d = dg.make_desc(**self.fields)
         try:
             ws = dg.dg_gemm_workspace_size(d)
             return dg.dg_gemm_describe(d, ws), d, ws
@@ -176,7 +180,7 @@ def sweep(p, steps, log):
                 if text is None or _kv(text)["splits"] != str(S):
                     continue
                 res["cands"].append((tile, sched, S, t.time(d, ws)))
-    os.environ.pop("DG_FORCE_TILE", None)
+    os.environ.pop("DG_FORCE_PLAN", None)
     os.environ.pop("DG_TUNED", None)
     best = min(res["cands"], key=lambda c: c[3])
     if best[3] < res["heuristic_us"] * (1.0 - MARGIN):

@@ -109,7 +109,18 @@ typedef enum {
  * automatic choice uses it only for those kernels, when there is at least
  * one full wave of tiles, the last wave would be less than 85 % full,
  * K >= 2048 and the caller passes enough workspace, or where the
- * offline-tuned plan table names it for the exact shape. */
+ * offline-tuned plan table names it for the exact shape.
+ *
+ * With schedule, algo and split_k all left to the library, an output whose
+ * N ends 1 to 8 columns past a whole number of tile columns (for the tile
+ * the plan chose), with row-major A whose rows are 16-byte aligned and at
+ * least one full-width tile per compute unit, is computed in two launches
+ * on the stream: the tiled plan over the full tile columns, then a small
+ * kernel over the last columns (one wavefront per row of A, each output a
+ * K-long fp32 dot product, the same epilogue).  A tuned stream-K plan with
+ * a tail wave keeps the whole grid instead.  Results agree with the single
+ * tiled plan within the dtype's tolerance (bit for bit when every product
+ * and partial sum is exact in fp32). */
 typedef enum {
     DG_SCHED_AUTO = 0,
     DG_SCHED_DATA_PARALLEL = 1,
@@ -199,7 +210,9 @@ dg_status dg_gemm(const dg_gemm_desc *d, const void *A, const void *B, void *C,
 /* Write a one-line, NUL-terminated description of the plan dg_gemm would
  * run for `d` (kernel, tile, split, grid, workspace) into buf[len].  Pass
  * workspace_bytes as dg_gemm would receive it (it decides split-K when
- * split_k == 0).  "tuned=1" marks a plan taken from the library's
+ * split_k == 0).  "sliver=n" (n > 0) marks the two-launch split above:
+ * the rest of the line then describes the tiled plan over the first N - n
+ * columns.  "tuned=1" marks a plan taken from the library's
  * offline-tuned table: for the exact (kernel family, M, N, K, batch) of a
  * shape swept on an MI355X, the tile and schedule that measured fastest
  * replace the heuristic choice ("GEMM Kernel Optimization", Autotuning,

@@ -184,7 +184,11 @@ def test_plans_of_the_five_workloads(monkeypatch):
     c3 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c3"]))
     assert "kernel=mfma_bf16" in c3 and "bm=256 bn=256" in c3 and "programs=256" in c3
     c4 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c4"]))
-    assert "kernel=mfma_bf16" in c4 and "bm=128 bn=128" in c4    # 272 tiles of 256^2 quantise badly
+    # 272 tiles of 256^2 quantise badly, so the full plan takes 128^2 tiles;
+    # N = 4097 leaves one column past the last full one: the full columns
+    # (32 x 32 tiles of 128^2, two waves) run tiled, the last one as a sliver
+    assert "kernel=mfma_bf16" in c4 and "bm=128 bn=128" in c4 and "programs=1024" in c4
+    assert "sliver=1" in c4 and "schedule=data_parallel" in c4
     d5 = _desc_for(W.WORKLOADS["c5"])
     ws = dg.dg_gemm_workspace_size(d5)
     assert ws > 0
@@ -192,17 +196,24 @@ def test_plans_of_the_five_workloads(monkeypatch):
     assert "kernel=mfma_bf16" in c5 and "splits=1 " not in c5
     # without workspace the automatic choice does not split
     assert "splits=1 " in dg.dg_gemm_describe(d5, 0)
-    # the tuned plan of the ragged GELU GEMM: the table's tile with stream-K
-    # when workspace is given, data-parallel on the same tile without
+    # the tuned plan of the ragged GELU GEMM: a stream-K entry keeps the
+    # whole grid (its tail wave sliced) when workspace is given; without
+    # workspace, or with a data-parallel entry, the entry plans the full
+    # columns and the last column is a sliver
     monkeypatch.delenv("DG_TUNED")
     p4 = W.WORKLOADS["c4"]
     entry = [e for e in _tuned_entries() if e[:5] == ("KERNEL_MFMA_BF16", p4.M, p4.N, p4.K, 1)]
-    assert len(entry) == 1 and entry[0][6] == "DG_SCHED_STREAM_K"
+    assert len(entry) == 1
     d4 = _desc_for(p4)
     t4 = dg.dg_gemm_describe(d4, dg.dg_gemm_workspace_size(d4))
-    assert "tuned=1" in t4 and f"tile={entry[0][5]} " in t4 and "schedule=stream_k" in t4
+    assert "tuned=1" in t4 and f"tile={entry[0][5]} " in t4
+    if entry[0][6] == "DG_SCHED_STREAM_K":
+        assert "schedule=stream_k" in t4 and "sliver=0" in t4
+    else:
+        assert "schedule=data_parallel" in t4 and "sliver=1" in t4
     t4 = dg.dg_gemm_describe(d4, 0)
-    assert "tuned=1" in t4 and f"tile={entry[0][5]} " in t4 and "schedule=data_parallel" in t4
+    assert "tuned=1" in t4 and f"tile={entry[0][5]} " in t4
+    assert "schedule=data_parallel" in t4 and "sliver=1" in t4
 
 
 def test_f16_plans():
@@ -227,7 +238,8 @@ def test_f16_plans():
     assert _gemm_status(_desc(a_type="f16", b_type="f16", c_type="f16"), C=PC + 1) == \
         dg.DG_ERROR_INVALID_VALUE
     # forced stream-K on the fp16 kernel
-    sk = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["f16_gelu"].replace(K=4096)),
+    # (N = 4352: 16 x 17 tiles of 256^2, no sliver columns, a thin last wave)
+    sk = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["f16_gelu"].replace(K=4096, N=4352)),
                              1 << 34)
     assert "kernel=mfma_f16" in sk and "schedule=stream_k" in sk and "bm=256" in sk
 
@@ -267,13 +279,14 @@ def _sk_fields(text):
 
 
 def test_stream_k_plan_for_a_badly_quantised_grid(monkeypatch):
-    # the heuristic (tuned table off) on the GELU workload's grid with a long
-    # K (the automatic choice wants K >= 2048)
+    # the heuristic (tuned table off) on a grid like the GELU workload's
+    # with a long K (the automatic choice wants K >= 2048) and N = 4352, so
+    # that no sliver columns are split off
     monkeypatch.setenv("DG_TUNED", "0")
-    d = _desc_for(W.WORKLOADS["c4"].replace(K=4096))
+    d = _desc_for(W.WORKLOADS["c4"].replace(K=4096, N=4352))
     ws = dg.dg_gemm_workspace_size(d)
     text = dg.dg_gemm_describe(d, ws)
-    # with stream-K taking the tail wave the large tile is kept: 4095 x 4097
+    # with stream-K taking the tail wave the large tile is kept: 4095 x 4352
     # in 256 x 256 tiles = 16 x 17 = 272 = one wave of 256 + 16 tail tiles
     assert "schedule=stream_k" in text and "bm=256 bn=256" in text
     sk = _sk_fields(text)
@@ -353,9 +366,13 @@ def test_tuned_table_entries_are_what_the_planner_picks(monkeypatch):
         text = dg.dg_gemm_describe(d, ws)
         assert "tuned=1" in text and f"tile={tile} " in text, (p.name, text)
         if sched == "DG_SCHED_DATA_PARALLEL":
-            assert "schedule=data_parallel" in text
-        if splits:
-            assert f"splits={splits} " in text
+            assert "schedule=data_parallel" in text, (p.name, text)
+            if splits:
+                assert f" splits={splits} " in text, (p.name, text)
+        else:
+            assert "schedule=stream_k" in text, (p.name, text)
+            if splits:
+                assert f"tail_splits={splits} " in text, (p.name, text)
         # DG_TUNED=0 gives the heuristic plan, DG_FORCE_TILE overrides the table
         monkeypatch.setenv("DG_TUNED", "0")
         assert "tuned=0" in dg.dg_gemm_describe(d, ws)

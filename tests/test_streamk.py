@@ -96,10 +96,11 @@ def test_stream_k_256_sampled(small_int, monkeypatch):
 
 
 def test_automatic_stream_k_matches_data_parallel():
-    # the GELU workload's ragged grid with a long K: the library's own plan
-    # (stream-K, with workspace) and the data-parallel plan agree bit for bit
-    # on small-integer inputs
-    p = W.WORKLOADS["c4"].replace(name="c4_longk", K=4096, act=W.ACT_NONE)
+    # a grid like the GELU workload's with a long K and N = 4352 (17 full
+    # tile columns, so no sliver columns): the library's own plan (stream-K,
+    # with workspace) and the data-parallel plan agree bit for bit on
+    # small-integer inputs
+    p = W.WORKLOADS["c4"].replace(name="c4_longk", K=4096, N=4352, act=W.ACT_NONE)
     x = W.make_inputs(p, small_int=True)
     dp1, t1 = _run(p, x)
     dp2, t2 = _run(p, x, schedule=dg.DG_SCHED_DATA_PARALLEL)
