@@ -222,6 +222,7 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
     constexpr int LPW = GROUPS / NW;             // ... per wave
     constexpr int STAGE_SLOTS = ROWS * CPR;      // 16-byte slots per stage
     constexpr int D = kStages - 1;               // prefetch distance (tiles)
+    static_assert((D - 1) * LPW <= 63, "loads left in flight fit the vmcnt counter");
     static_assert(MBK == 32 || MBK == 64, "stage K width");
     static_assert(KS % 2 == 0, "fragment sets alternate per k-step");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
