@@ -550,8 +550,10 @@ dg_status make_call_plan(const dg_gemm_desc *d, const void *A, const void *B, si
     if (!tiled || (p.tuned && p.sk.tail_tiles > 0) || d->algo != DG_ALGO_AUTO ||
         d->schedule != DG_SCHED_AUTO || d->split_k != 0 ||
         !reads_ab(d) || d->a_order != DG_ROW_MAJOR ||
-        (d->lda * elem_size(d->a_type)) % 16 != 0 || (A && !aligned_to(A, 16)))
-        return DG_SUCCESS;
+        (d->lda * elem_size(d->a_type)) % 16 != 0 ||
+        (d->batch > 1 && (d->stride_a * elem_size(d->a_type)) % 16 != 0) ||
+        (A && !aligned_to(A, 16)))
+        return DG_SUCCESS;     // the sliver kernel reads A's rows in aligned 16-byte pieces
     const int64_t nrem = d->N % p.tile.bn;
     const int64_t n_main = d->N - nrem;
     if (nrem == 0 || nrem > kMaxSliver || n_main < p.tile.bn ||
