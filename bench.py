@@ -358,6 +358,28 @@ def cpu_baseline(name, budget_s=12.0):
                       f"product plus epilogue), {el:.1f} s"}
 
 
+def _roofline(workload, r):
+    """The roofline object of one timed workload: algorithmic flops (or, for
+    an HBM-bound kernel, bytes) per call over the measured time per call,
+    against the kernel's published peak, and the profiled HBM traffic."""
+    from dense_gemm_10_amd import accounting as acc
+    p = r["problem"]
+    bound, peak = _roofline_peak(p, r["kernel"])
+    if bound == "hbm":
+        achieved = acc.problem_bytes(p) / (r["ms"] * 1e-3)
+        roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": peak / 1e9, "unit": "GB/s",
+                "frac": achieved / peak}
+    else:
+        achieved = p.flops() / (r["ms"] * 1e-3)
+        roof = {"bound": bound, "achieved": achieved / 1e12, "peak": peak / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / peak}
+    roof["traffic"] = traffic_for(workload)
+    roof["kernel"] = r["kernel"]
+    roof["algorithmic_bytes"] = acc.problem_bytes(p)
+    roof["algorithmic_flops"] = p.flops()
+    return roof
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,32 +434,17 @@ def main():
     overrides = dict(algo=args.algo, group_m=args.group_m, xcd_remap=args.xcd_remap)
     main_r = time_workload(args.workload, args.steps, args.warmup, **overrides)
     p = main_r["problem"]
-    bound, peak = _roofline_peak(p, main_r["kernel"])
     published = acc.compute_peak_for(p)
-    if bound == "hbm":
-        achieved = acc.problem_bytes(p) / (main_r["ms"] * 1e-3)
-        roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": peak / 1e9, "unit": "GB/s",
-                "frac": achieved / peak, "traffic": None}
-    else:
-        achieved = p.flops() / (main_r["ms"] * 1e-3)
-        roof = {"bound": bound, "achieved": achieved / 1e12, "peak": peak / 1e12,
-                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None}
-    traffic = traffic_for(args.workload)
-    roof["traffic"] = traffic
-    roof["kernel"] = main_r["kernel"]
-    roof["algorithmic_bytes"] = acc.problem_bytes(p)
-    roof["algorithmic_flops"] = p.flops()
+    roof = _roofline(args.workload, main_r)
 
     secondary = None
     if args.secondary != "none" and args.secondary != args.workload:
         s = time_workload(args.secondary, args.steps, args.warmup, **overrides)
         sp = s["problem"]
-        sb, spk = _roofline_peak(sp, s["kernel"])
         secondary = {"workload": sp.name, "value": s["tflops"], "unit": "TFLOPS",
                      "ms_per_step": s["ms"], "dtype": _dtype_name(sp), "plan": s["plan"],
                      "frac_of_published_peak": s["tflops"] * 1e12 / acc.compute_peak_for(sp),
-                     "roofline": {"bound": sb, "peak": spk / 1e12 if sb != "hbm" else spk / 1e9,
-                                  "unit": "TFLOP/s" if sb != "hbm" else "GB/s"}}
+                     "roofline": _roofline(args.secondary, s)}
         del s
 
     cpu = None
