@@ -170,11 +170,12 @@ def sweep(p, steps, log):
                 continue
             if sched != "data_parallel" or p.split_k:
                 continue
-            # explicit split-K counts when the tiles leave compute units idle
+            # explicit split-K counts when the tiles leave compute units idle (at
+            # least 64 of K per slice)
             text1, _, _ = t.plan(tile=tile, schedule=1, split_k=1)
             tiles = int(_kv(text1)["programs"])
             for S in (2, 4, 8, 16):
-                if tiles >= 256 or tiles * S > 1024 or p.K < 256 * S:
+                if tiles >= 256 or tiles * S > 1024 or p.K < 64 * S:
                     continue
                 text, d, ws = t.plan(tile=tile, schedule=1, split_k=S)
                 if text is None or _kv(text)["splits"] != str(S):
