@@ -527,7 +527,8 @@ struct CallPlan {
 // tiles of its last column hold one valid column each.  When the library
 // chooses the schedule (no split-K or schedule asked for), the plan's tile
 // leaves 1 .. kMaxSliver columns past the last full tile column, the full
-// columns alone make at least one tile per compute unit, and A is
+// columns alone make at least one tile per compute unit and one wave fewer
+// than the whole grid (waves of per-CU occupancy x 256 tiles), and A is
 // row-major with 16-byte aligned rows, the call runs the tiled plan on the
 // full columns and the sliver kernel on the rest.  The full columns' plan
 // is looked up in the tuned table under the caller's shape; without an
@@ -556,8 +557,15 @@ dg_status make_call_plan(const dg_gemm_desc *d, const void *A, const void *B, si
         return DG_SUCCESS;     // the sliver kernel reads A's rows in aligned 16-byte pieces
     const int64_t nrem = d->N % p.tile.bn;
     const int64_t n_main = d->N - nrem;
-    if (nrem == 0 || nrem > kMaxSliver || n_main < p.tile.bn ||
-        ceil_div(d->M, p.tile.bm) * (n_main / p.tile.bn) * d->batch < kNumCu)
+    if (nrem == 0 || nrem > kMaxSliver || n_main < p.tile.bn)
+        return DG_SUCCESS;
+    // Only where the last tile column costs a wave of its own: the sliver
+    // kernel reads all of A once (8 MB on the GELU problem, but 71 MB for
+    // 4352 x 4353 x 8192, whose grid keeps its wave count without the column).
+    const int64_t rows = ceil_div(d->M, p.tile.bm) * d->batch;
+    const int64_t slots = kNumCu * (p.tile.per_cu > 0 ? p.tile.per_cu : 1);
+    const int64_t tiles_main = rows * (n_main / p.tile.bn);
+    if (tiles_main < kNumCu || ceil_div(tiles_main, slots) == ceil_div(tiles_main + rows, slots))
         return DG_SUCCESS;
     dg_gemm_desc m = *d;
     m.N = n_main;
