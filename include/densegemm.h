@@ -113,8 +113,9 @@ typedef enum {
  *
  * With schedule, algo and split_k all left to the library, an output whose
  * N ends 1 to 8 columns past a whole number of tile columns (for the tile
- * the plan chose), with row-major A whose rows are 16-byte aligned and at
- * least one full-width tile per compute unit, is computed in two launches
+ * the plan chose), with row-major A whose rows are 16-byte aligned, at
+ * least one full-width tile per compute unit, and one wave of tiles fewer
+ * without the last tile column, is computed in two launches
  * on the stream: the tiled plan over the full tile columns, then a small
  * kernel over the last columns (one wavefront per row of A, each output a
  * K-long fp32 dot product, the same epilogue).  A tuned stream-K plan with
