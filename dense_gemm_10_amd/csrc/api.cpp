@@ -253,7 +253,7 @@ const TileConfig *tile_named(const TileConfig *table, int n, const char *name)
 // entry is.  False when unset or when the tile is not in `table`.
 bool forced_plan(const TileConfig *table, int n, Kernel k, TunedEntry *out)
 {
-    static char name[96];
+    thread_local static char name[96];   // the entry points at it; one per planning thread
     const char *env = getenv("DG_FORCE_PLAN");
     if (!env)
         return false;
