@@ -43,8 +43,8 @@ def _dtype_name(p):
 
 def _roofline_peak(p, kernel):
     """(bound, peak) of the workload's dominant kernel: its compute peak
-    (matrix cores for the MFMA kernels, the unpacked vector-FMA rate for
-    the others), or HBM when the algorithmic bytes take longer at 8 TB/s
+    (matrix cores for the MFMA kernels, the fp32 vector-FMA rate for the
+    others), or HBM when the algorithmic bytes take longer at 8 TB/s
     than the flops at that peak."""
     from dense_gemm_10_amd import accounting as acc
     if kernel.startswith("mfma_bf16"):
@@ -54,38 +54,152 @@ def _roofline_peak(p, kernel):
     elif kernel.startswith("mfma_f32"):
         bound, peak = "mfma", acc.PEAK_F32
     else:
-        bound, peak = "alu", acc.PEAK_F32_VALU_UNPACKED
+        bound, peak = "alu", acc.PEAK_F32_VALU
     if acc.problem_bytes(p) / acc.PEAK_HBM > acc.problem_flops(p) / peak:
         return "hbm", acc.PEAK_HBM
     return bound, peak
 
 
-def time_workload(name, steps, warmup, **desc_overrides):
-    """Run one workload: returns dict with ms/step, TFLOPS, plan string."""
+def _event_pair():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+class Flusher:
+    """Reads a 512 MiB device buffer (a sum): evicts the L2s and the 256 MB
+    Infinity Cache (MALL) between calls with clean lines, so that the next
+    call reads its operands from HBM (a cold-cache measurement) without
+    also paying for the write-back of a flush written to memory."""
+
+    def __init__(self, nbytes=512 << 20):
+        import torch
+        self.buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        self.sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        import torch
+        torch.sum(self.buf, 0, keepdim=True, out=self.sink)
+
+
+def run_window(dp, stream, steps, flush=None):
+    """`steps` timed calls.  Returns (window ms per call, per-call ms list):
+    the window time runs from the first call's start event to the last
+    call's end event (launch gaps included), divided by `steps`; each call
+    also has its own event pair.  With `flush`, the flush runs before each
+    call, outside its event pair, and the window time is the sum of the
+    pairs."""
+    import torch
+    pairs = [_event_pair() for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s, e in pairs:
+        if flush is not None:
+            flush()
+        s.record(stream)
+        dp.run(stream.cuda_stream)
+        e.record(stream)
+    torch.cuda.synchronize()
+    per_call = [s.elapsed_time(e) for s, e in pairs]
+    if flush is not None:
+        window = sum(per_call) / steps
+    else:
+        window = pairs[0][0].elapsed_time(pairs[-1][1]) / steps
+    return window, per_call
+
+
+def _smi_gfx_clocks():
+    """Current shader clock of each XCD (MHz) from amd-smi, or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        d = json.loads(r.stdout)
+        clk = d["gpu_data"][0]["clock"] if isinstance(d, dict) else d[0]["clock"]
+        return [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_")]
+    except Exception:        # no amd-smi, or another output format
+        return None
+
+
+def clock_window(dp, stream, seconds=2.5):
+    """Keep the GPU busy with back-to-back calls for `seconds` while a
+    thread samples the XCD clocks with amd-smi; returns the samples (one
+    list of per-XCD MHz each)."""
+    import threading
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            c = _smi_gfx_clocks()
+            if c is None:
+                return
+            samples.append(c)
+
+    t = threading.Thread(target=sampler, daemon=True)
+    batches = []
+    t0 = time.perf_counter()
+    t.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            dp.run(stream.cuda_stream)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        batches.append(ev)
+        if len(batches) > 2:
+            batches.pop(0).synchronize()
+    stop.set()
+    torch.cuda.synchronize()
+    t.join(timeout=30)
+    # amd-smi reports a stale idle reading (~0.1-0.2 GHz) until the clock
+    # has risen: keep the samples taken under load
+    return [c for c in samples[1:] if min(c) >= 500]
+
+
+def _window_stats(window_ms, per_call):
+    srt = sorted(per_call)
+    return {"ms_per_step": window_ms, "kernel_ms_mean": sum(per_call) / len(per_call),
+            "kernel_ms_min": srt[0], "kernel_ms_median": srt[len(srt) // 2],
+            "kernel_ms_max": srt[-1], "calls": len(per_call)}
+
+
+def time_workload(name, steps, warmup, settle=0, steps_sustained=0, flush=None, clock_s=0.0,
+                  **overrides):
+    """Run one workload through dg_gemm: `warmup` untimed calls, a timed
+    window of `steps` calls, then (settle > 0) `settle` more untimed calls
+    and a second timed window of `steps_sustained` calls, the sustained
+    rate once the clock has met the power limit.  With `flush` (cold
+    caches), the flush runs before every call of the timed windows."""
     import torch
     import workloads as W
     from workloads.device import DeviceProblem
     p = W.WORKLOADS[name]
     log(f"[bench] {name}: generating {p.name}")
     x = W.make_inputs(p)
-    dp = DeviceProblem(p, x, **desc_overrides)
+    dp = DeviceProblem(p, x, **overrides)
     plan = dp.describe()
     log(f"[bench] {name}: plan {plan}")
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         dp.run(stream.cuda_stream)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        dp.run(stream.cuda_stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
-    flops = p.flops()
-    return dict(problem=p, inputs=x, ms=ms, tflops=flops / (ms * 1e-3) / 1e12, plan=plan,
-                kernel=plan.split()[0].split("=")[1])
+    w, per = run_window(dp, stream, steps, flush)
+    out = dict(problem=p, plan=plan, kernel=plan.split()[0].split("=")[1],
+               window=_window_stats(w, per), inputs=x)
+    out["ms"] = w
+    out["kernel_ms"] = out["window"]["kernel_ms_mean"]
+    out["tflops"] = p.flops() / (w * 1e-3) / 1e12
+    if settle > 0 and steps_sustained > 0:
+        for _ in range(settle):
+            dp.run(stream.cuda_stream)
+        w2, per2 = run_window(dp, stream, steps_sustained, flush)
+        out["sustained"] = _window_stats(w2, per2)
+    if clock_s > 0:
+        smp = clock_window(dp, stream, clock_s)
+        if smp:
+            flat = [v for c in smp for v in c]
+            out["clock_mhz"] = {"samples": smp, "mean": sum(flat) / len(flat),
+                                "min": min(flat), "max": max(flat),
+                                "source": "amd-smi metric -c, per XCD, during back-to-back calls"}
+    del dp
+    return out
 
 
 def time_copy(steps, warmup, nbytes=512 << 20):
@@ -112,6 +226,7 @@ def time_copy(steps, warmup, nbytes=512 << 20):
 
 
 PROFILES = os.path.join(ROOT, "profiles")
+N_XCD = 8          # MI355X: 8 XCDs of 32 compute units
 
 
 def kernel_source_hash():
@@ -147,24 +262,50 @@ def _csv_rows(outdir, suffix):
         return list(csv.DictReader(f))
 
 
-# Default timed calls and warmup.  The clock settles over the first ~20 ms
-# of a fresh run (the fp32 4096^3 call falls from ~1.27 ms to ~1.07 ms over
-# its first 20 calls), so the default warmup covers that before the timed
-# calls; the kernel-trace pass of --collect-profile runs the same counts.
-DEFAULT_STEPS = 50
-DEFAULT_WARMUP = 30
+# Default timed calls and warmup: the counts the benchmark is run with at
+# the end of every build cycle (python3 bench.py --gpus 1 --steps 20
+# --warmup 5), so that a plain run and the kernel-trace pass of
+# --collect-profile time the same windows.  The chip's clock moves with its
+# power state over the first calls of a fresh process (the fp32 4096^3 call
+# falls from ~1.27 ms to ~1.0 ms over its first ~20 calls; the bf16 4096^3
+# call runs ~110 us for ~17 calls, then 125-145 us once the power limit
+# applies), so every workload also gets a second, sustained window of
+# max(K, SUSTAINED_MIN) calls after SETTLE further untimed calls.
+DEFAULT_STEPS = 20
+DEFAULT_WARMUP = 5
+SETTLE = 300
+SUSTAINED_MIN = 50
+CLOCK_S = 2.5      # seconds of back-to-back calls while amd-smi samples the clocks
 
 
-def _timed_means(out, warmup):
-    """Mean duration (ns) per kernel over its dispatches after the first
-    `warmup` (the bench's timed calls), from a --kernel-trace CSV."""
+def _sustained_steps(steps):
+    return max(steps, SUSTAINED_MIN)
+
+
+def _timed_means(out, warmup, steps, settle):
+    """Mean duration (ns) per kernel over its dispatches in the bench's two
+    timed windows: dispatches [warmup, warmup + steps) (first window) and,
+    after `settle` more, the next _sustained_steps(steps) (sustained
+    window), from a --kernel-trace CSV.  Every call dispatches each of its
+    kernels once, so a kernel's n-th dispatch belongs to the n-th call."""
     import collections
     rows = sorted(_csv_rows(out, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
     per = collections.defaultdict(list)
     for r in rows:
         per[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    return [{"Name": k, "Calls": len(v) - warmup, "AverageNs": sum(v[warmup:]) / (len(v) - warmup)}
-            for k, v in per.items() if len(v) > warmup]
+    res = []
+    s0 = warmup + steps + settle
+    s1 = s0 + _sustained_steps(steps)
+    for k, v in per.items():
+        if len(v) < warmup + steps:
+            continue
+        first = v[warmup:warmup + steps]
+        r = {"Name": k, "Calls": len(first), "AverageNs": sum(first) / len(first)}
+        if settle > 0 and len(v) >= s1:
+            r["SustainedCalls"] = s1 - s0
+            r["SustainedAverageNs"] = sum(v[s0:s1]) / (s1 - s0)
+        res.append(r)
+    return res
 
 
 def _per_dispatch(rows, name_filter):
@@ -188,7 +329,8 @@ def _shown(cmd, tmp):
     return text.replace(tmp, "$OUT")
 
 
-def collect_profile(workload, tmp, out_dir=PROFILES, knobs=()):
+def collect_profile(workload, tmp, out_dir=PROFILES, knobs=(), steps=DEFAULT_STEPS,
+                    warmup=DEFAULT_WARMUP):
     """Kernel-trace statistics, HBM traffic and L2 hit counters of one
     workload, written to profiles/.  FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch) are each scaled by the ratio between the bytes a plain device
@@ -197,23 +339,27 @@ def collect_profile(workload, tmp, out_dir=PROFILES, knobs=()):
     `knobs` are extra bench.py arguments for the profiled runs (tile order,
     kernel family)."""
     import subprocess
-    child = ["--workload", workload, "--secondary", "none", "--no-cpu-baseline"] + list(knobs)
+    child = ["--workload", workload, "--secondary", "none", "--no-extras",
+             "--no-cpu-baseline", "--clock-seconds", "0"] + list(knobs)
+    short = ["--steps", "3", "--warmup", "1", "--settle", "0"]   # counter passes
     results = {}
-    # 1. kernel trace with statistics
+    # 1. kernel trace with statistics, the bench's own windows
     out = os.path.join(tmp, "trace")
     cmd = _rocprof(["--kernel-trace", "--stats"], out) + child + [
-        "--steps", str(DEFAULT_STEPS), "--warmup", str(DEFAULT_WARMUP)]
+        "--steps", str(steps), "--warmup", str(warmup)]
     log(f"[profile] {' '.join(cmd)}")
     subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL)
     stats = _csv_rows(out, "kernel_stats.csv")
     results["trace_command"] = _shown(cmd, tmp)
     results["kernel_stats"] = [{k: r[k] for k in ("Name", "Calls", "AverageNs", "MinNs", "MaxNs",
                                                  "Percentage")} for r in stats]
-    results["timed_means"] = _timed_means(out, DEFAULT_WARMUP)
+    results["timed_means"] = _timed_means(out, warmup, steps, SETTLE)
+    results["windows"] = {"warmup": warmup, "steps": steps, "settle": SETTLE,
+                          "sustained_steps": _sustained_steps(steps)}
     # 2. traffic counters, GEMM and copy calibration
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         out = os.path.join(tmp, counter)
-        cmd = _rocprof(["--pmc", counter], out) + child + ["--steps", "3", "--warmup", "1"]
+        cmd = _rocprof(["--pmc", counter], out) + child + short
         log(f"[profile] {' '.join(cmd)}")
         subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL)
         kib, n = _per_dispatch(_csv_rows(out, "counter_collection.csv"), "gemm_")
@@ -229,8 +375,7 @@ def collect_profile(workload, tmp, out_dir=PROFILES, knobs=()):
                             "command": _shown(cmd, tmp), "copy_command": _shown(cmd_c, tmp)}
     # 3. L2 (TCC) hits and misses of the GEMM kernels
     out = os.path.join(tmp, "tcc")
-    cmd = _rocprof(["--pmc", "TCC_HIT_sum", "TCC_MISS_sum"], out) + child + ["--steps", "3",
-                                                                           "--warmup", "1"]
+    cmd = _rocprof(["--pmc", "TCC_HIT_sum", "TCC_MISS_sum"], out) + child + short
     log(f"[profile] {' '.join(cmd)}")
     subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL)
     rows = _csv_rows(out, "counter_collection.csv")
@@ -243,8 +388,7 @@ def collect_profile(workload, tmp, out_dir=PROFILES, knobs=()):
     # of CU cycles, LDS bank-conflict cycles per LDS cycle (rocprofv3's
     # derived metrics; 4 SQ counters and 1 GRBM counter in one pass)
     out = os.path.join(tmp, "util")
-    cmd = _rocprof(["--pmc", "MfmaUtil", "VALUBusy", "LdsBankConflict"], out) + child + [
-        "--steps", "3", "--warmup", "1"]
+    cmd = _rocprof(["--pmc", "MfmaUtil", "VALUBusy", "LdsBankConflict"], out) + child + short
     log(f"[profile] {' '.join(cmd)}")
     subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL)
     rows = _csv_rows(out, "counter_collection.csv")
@@ -254,6 +398,24 @@ def collect_profile(workload, tmp, out_dir=PROFILES, knobs=()):
         util[name] = _per_dispatch(sel, "gemm_")[0] if sel else None
     util["command"] = _shown(cmd, tmp)
     results["utilisation"] = util
+    # 5. effective shader clock during the GEMM dispatches: GPU-busy cycles
+    # (GRBM_GUI_ACTIVE, summed over the XCDs) per XCD over the dispatch's
+    # duration
+    out = os.path.join(tmp, "clock")
+    cmd = _rocprof(["--pmc", "GRBM_GUI_ACTIVE"], out) + child + short
+    log(f"[profile] {' '.join(cmd)}")
+    subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL)
+    rows = [r for r in _csv_rows(out, "counter_collection.csv") if "gemm_" in r["Kernel_Name"]]
+    clocks = []
+    for r in rows:
+        try:
+            dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        except (KeyError, ValueError):
+            dur = 0
+        if dur > 0:
+            clocks.append(float(r["Counter_Value"]) / N_XCD / dur)
+    results["clock"] = {"ghz_per_dispatch": clocks, "command": _shown(cmd, tmp),
+                        "xcds": N_XCD}
     results["kernel_source_hash"] = kernel_source_hash()
     results["workload"] = workload
     results["knobs"] = list(knobs)
@@ -262,11 +424,20 @@ def collect_profile(workload, tmp, out_dir=PROFILES, knobs=()):
     return results
 
 
+def profile_tag(workload, knobs=()):
+    """File tag of a profile: the workload, then any knobs (e.g. c2_algo2)."""
+    k = list(knobs)
+    extra = "".join(f"_{k[i].lstrip('-').replace('-', '')}{k[i + 1]}"
+                    for i in range(0, len(k) - 1, 2))
+    return workload + extra
+
+
 def write_profile(results, out_dir=PROFILES):
-    """Write traffic_<workload>.json and a markdown summary of `results`."""
+    """Write traffic_<tag>.json and a markdown summary of `results`."""
     workload = results["workload"]
+    tag = profile_tag(workload, results.get("knobs", []))
     os.makedirs(out_dir, exist_ok=True)
-    with open(os.path.join(out_dir, f"traffic_{workload}.json"), "w") as f:
+    with open(os.path.join(out_dir, f"traffic_{tag}.json"), "w") as f:
         json.dump(results, f, indent=1)
     import workloads as W
     p = W.WORKLOADS[workload]
@@ -284,12 +455,19 @@ def write_profile(results, out_dir=PROFILES):
                      f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | "
                      f"{float(r['Percentage']):.2f} |")
     if results.get("timed_means"):
+        w = results.get("windows", {"warmup": DEFAULT_WARMUP, "steps": DEFAULT_STEPS,
+                                    "settle": 0, "sustained_steps": 0})
         lines += ["", "The statistics above cover every dispatch, warmup included. Over the "
-                  "timed calls only (the dispatches after each kernel's first "
-                  f"{DEFAULT_WARMUP}), the same trace gives:", "",
-                  "| kernel | timed calls | average ns |", "|---|---|---|"]
+                  "bench's timed windows only (first window: each kernel's dispatches "
+                  f"{w['warmup']} .. {w['warmup'] + w['steps'] - 1}; sustained window: the "
+                  f"{w['sustained_steps']} dispatches after {w['settle']} further untimed "
+                  "ones), the same trace gives:", "",
+                  "| kernel | first window calls | average ns | sustained calls | "
+                  "sustained average ns |", "|---|---|---|---|---|"]
         for r in results["timed_means"]:
-            lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {r['AverageNs']:.0f} |")
+            sus = (f"{r['SustainedCalls']} | {r['SustainedAverageNs']:.0f}"
+                   if "SustainedCalls" in r else "- | -")
+            lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {r['AverageNs']:.0f} | {sus} |")
     lines += ["", "## HBM traffic per GEMM dispatch", "",
               "| counter | KiB / dispatch | copy calibration KiB (512 MiB copy) | scale | bytes |",
               "|---|---|---|---|---|"]
@@ -308,33 +486,55 @@ def write_profile(results, out_dir=PROFILES):
                   "LdsBankConflict (conflict cycles per LDS cycle) |", "|---|---|---|",
                   f"| {fmt(u['MfmaUtil'], '{:.1f}')} | {fmt(u['VALUBusy'], '{:.1f}')} | "
                   f"{fmt(u['LdsBankConflict'], '{:.4f}')} |", "", f"Command: `{u['command']}`", ""]
+    if results.get("clock", {}).get("ghz_per_dispatch"):
+        c = results["clock"]
+        g = ", ".join(f"{v:.3f}" for v in c["ghz_per_dispatch"])
+        lines += ["## Effective shader clock per GEMM dispatch", "",
+                  f"GRBM_GUI_ACTIVE / {c['xcds']} XCDs / dispatch duration: {g} GHz", "",
+                  f"Command: `{c['command']}`", ""]
     if "L2" in results:
         l2 = results["L2"]
         lines += ["## L2 (TCC) hit rate per GEMM dispatch", "",
                   "| TCC_HIT | TCC_MISS | hit rate |", "|---|---|---|",
                   f"| {l2['hits_per_dispatch']:.0f} | {l2['misses_per_dispatch']:.0f} | "
                   f"{l2['hit_rate']:.3f} |", "", f"Command: `{l2['command']}`", ""]
-    with open(os.path.join(out_dir, f"{workload}_{p.name}.md"), "w") as f:
+    with open(os.path.join(out_dir, f"{tag}_{p.name}.md"), "w") as f:
         f.write("\n".join(lines))
 
 
-def traffic_for(workload):
+def traffic_for(workload, knobs=()):
     """HBM bytes per launch from profiles/, or None when missing or taken
     with other kernel sources."""
-    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    path = os.path.join(PROFILES, f"traffic_{profile_tag(workload, knobs)}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
-    if t.get("knobs") or t.get("library", "in-tree") != "in-tree":
+    if list(t.get("knobs", [])) != list(knobs) or t.get("library", "in-tree") != "in-tree":
         return None      # taken with another tile order, family or build
     return t["FETCH_SIZE"]["bytes_per_dispatch"] + t["WRITE_SIZE"]["bytes_per_dispatch"]
 
 
+def host_cpu():
+    """CPU model and the cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "cores_available": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(name, budget_s=12.0):
-    """Oracle throughput on a seeded sample of the workload's outputs."""
+    """Oracle throughput on a seeded sample of the workload's outputs, on
+    every core; and the whole 256^3 workload (all of its outputs) on one
+    core."""
     import numpy as np
     import oracle
     import workloads as W
@@ -352,32 +552,66 @@ def cpu_baseline(name, budget_s=12.0):
         chunk = min(chunk * 2, 262144)
     el = time.perf_counter() - t0
     flops = 2.0 * p.K * done
-    return {"value": flops / el / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": f"{done} seeded output elements of {p.name} (each a K={p.K} fp64 dot "
-                      f"product plus epilogue), {el:.1f} s"}
+    out = {"value": flops / el / 1e12, "unit": "TFLOPS", "cores": oracle.max_threads(),
+           "kind": "oracle",
+           "sample": f"{done} seeded output elements of {p.name} (each a K={p.K} fp64 dot "
+                     f"product plus epilogue), {el:.1f} s"}
+    p1 = W.WORKLOADS["c1"]
+    x1 = W.make_inputs(p1)
+    t0 = time.perf_counter()
+    oracle.gemm(p1, x1.A, x1.B, x1.C, x1.bias, nthreads=1)
+    el1 = time.perf_counter() - t0
+    out["one_core_full"] = {"workload": p1.name, "seconds": el1,
+                            "gflops": p1.flops() / el1 / 1e9, "cores": 1}
+    out["host"] = host_cpu()
+    return out
 
 
-def _roofline(workload, r):
+def _roofline(workload, r, ms=None, knobs=()):
     """The roofline object of one timed workload: algorithmic flops (or, for
-    an HBM-bound kernel, bytes) per call over the measured time per call,
-    against the kernel's published peak, and the profiled HBM traffic."""
+    an HBM-bound kernel, bytes) per call over the measured kernel time per
+    call (the mean of per-call HIP event pairs on the launch stream, unless
+    `ms` is given), against the kernel's published peak, and the profiled
+    HBM traffic."""
     from dense_gemm_10_amd import accounting as acc
     p = r["problem"]
+    ms = r["kernel_ms"] if ms is None else ms
     bound, peak = _roofline_peak(p, r["kernel"])
     if bound == "hbm":
-        achieved = acc.problem_bytes(p) / (r["ms"] * 1e-3)
+        achieved = acc.problem_bytes(p) / (ms * 1e-3)
         roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": peak / 1e9, "unit": "GB/s",
                 "frac": achieved / peak}
     else:
-        achieved = p.flops() / (r["ms"] * 1e-3)
+        achieved = p.flops() / (ms * 1e-3)
         roof = {"bound": bound, "achieved": achieved / 1e12, "peak": peak / 1e12,
                 "unit": "TFLOP/s", "frac": achieved / peak}
-    roof["traffic"] = traffic_for(workload)
+    roof["traffic"] = traffic_for(workload, knobs)
     roof["kernel"] = r["kernel"]
+    roof["kernel_ms"] = ms
     roof["algorithmic_bytes"] = acc.problem_bytes(p)
     roof["algorithmic_flops"] = p.flops()
     return roof
+
+
+def _summary(workload, r, knobs=()):
+    """JSON record of one timed workload: both windows, plan and roofline
+    (of the sustained window when there is one)."""
+    from dense_gemm_10_amd import accounting as acc
+    p = r["problem"]
+    rec = {"workload": p.name, "key": workload, "plan": r["plan"], "dtype": _dtype_name(p),
+           "first_window": dict(r["window"], tflops=p.flops() / (r["ms"] * 1e-3) / 1e12)}
+    sus = r.get("sustained")
+    if sus:
+        rec["sustained"] = dict(sus, tflops=p.flops() / (sus["ms_per_step"] * 1e-3) / 1e12)
+        rec["roofline"] = _roofline(workload, r, sus["kernel_ms_mean"], knobs)
+        rec["roofline_first_window"] = _roofline(workload, r, None, knobs)
+    else:
+        rec["roofline"] = _roofline(workload, r, None, knobs)
+    rec["frac_of_published_peak"] = (rec.get("sustained", rec["first_window"])["tflops"] * 1e12
+                                     / acc.compute_peak_for(p))
+    if "clock_mhz" in r:
+        rec["clock_mhz"] = r["clock_mhz"]
+    return rec
 
 
 def main():
@@ -389,27 +623,37 @@ def main():
     ap.add_argument("--workload", default="c2", choices=list(W.WORKLOADS) + ["copy"])
     ap.add_argument("--secondary", default="c3",
                     help="second workload reported in the same line ('none' to skip)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the vector-FMA SGEMM leg and the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle", type=int, default=SETTLE,
+                    help="untimed calls between the first and the sustained window (0: no "
+                         "sustained window)")
+    ap.add_argument("--clock-seconds", type=float, default=CLOCK_S,
+                    help="seconds of back-to-back calls while amd-smi samples the clocks "
+                         "(0: skip)")
     ap.add_argument("--algo", type=int, default=0)
     ap.add_argument("--group-m", type=int, default=0)
     ap.add_argument("--xcd-remap", type=int, default=0)
     ap.add_argument("--collect-profile", action="store_true",
-                    help="run rocprofv3 (kernel trace, FETCH_SIZE, WRITE_SIZE) on this workload "
-                         "and write profiles/traffic_<workload>.json")
+                    help="run rocprofv3 (kernel trace, FETCH_SIZE, WRITE_SIZE, L2, utilisation) "
+                         "on this workload and write profiles/traffic_<tag>.json and a summary")
     ap.add_argument("--profile-dir", default=PROFILES,
                     help="where --collect-profile writes (default: profiles/)")
     args = ap.parse_args()
 
+    knobs = []
+    for flag, v in (("--algo", args.algo), ("--group-m", args.group_m),
+                    ("--xcd-remap", args.xcd_remap)):
+        if v:
+            knobs += [flag, str(v)]
+
     if args.collect_profile:
         import tempfile
-        knobs = []
-        for flag, v in (("--algo", args.algo), ("--group-m", args.group_m),
-                        ("--xcd-remap", args.xcd_remap)):
-            if v:
-                knobs += [flag, str(v)]
         with tempfile.TemporaryDirectory(dir=os.environ.get("TMPDIR", "/tmp")) as tmp:
-            r = collect_profile(args.workload, tmp, args.profile_dir, knobs)
-        print(json.dumps({"workload": args.workload,
+            r = collect_profile(args.workload, tmp, args.profile_dir, knobs, args.steps,
+                                args.warmup)
+        print(json.dumps({"workload": args.workload, "knobs": knobs,
                           "fetch_bytes": r["FETCH_SIZE"]["bytes_per_dispatch"],
                           "write_bytes": r["WRITE_SIZE"]["bytes_per_dispatch"]}), flush=True)
         return
@@ -432,20 +676,53 @@ def main():
         return
 
     overrides = dict(algo=args.algo, group_m=args.group_m, xcd_remap=args.xcd_remap)
-    main_r = time_workload(args.workload, args.steps, args.warmup, **overrides)
+    K, Wm, Ks = args.steps, args.warmup, _sustained_steps(args.steps)
+    ST, CS = args.settle, args.clock_seconds
+    main_r = time_workload(args.workload, K, Wm, ST, Ks, clock_s=CS, **overrides)
     p = main_r["problem"]
     published = acc.compute_peak_for(p)
-    roof = _roofline(args.workload, main_r)
+    roof = _roofline(args.workload, main_r, None, knobs)
+    main_sus = main_r.get("sustained")
+    if main_sus:
+        main_sus = dict(main_sus, tflops=p.flops() / (main_sus["ms_per_step"] * 1e-3) / 1e12,
+                        roofline=_roofline(args.workload, main_r, main_sus["kernel_ms_mean"],
+                                           knobs))
+    main_window = dict(main_r["window"])
+    del main_r["inputs"]
 
     secondary = None
     if args.secondary != "none" and args.secondary != args.workload:
-        s = time_workload(args.secondary, args.steps, args.warmup, **overrides)
-        sp = s["problem"]
-        secondary = {"workload": sp.name, "value": s["tflops"], "unit": "TFLOPS",
-                     "ms_per_step": s["ms"], "dtype": _dtype_name(sp), "plan": s["plan"],
-                     "frac_of_published_peak": s["tflops"] * 1e12 / acc.compute_peak_for(sp),
-                     "roofline": _roofline(args.secondary, s)}
+        s = time_workload(args.secondary, K, Wm, ST, Ks, clock_s=CS, **overrides)
+        rec = _summary(args.secondary, s, knobs)
+        # the sustained window is the value: the first window after a short
+        # warmup runs before the power limit applies
+        win = rec.get("sustained", rec["first_window"])
+        secondary = dict(rec, value=win["tflops"], unit="TFLOPS", ms_per_step=win["ms_per_step"])
         del s
+
+    extras = None
+    if not args.no_extras and not knobs:
+        extras = {}
+        if args.workload == "c2":
+            # the register-tiled vector-FMA SGEMM on the same problem
+            v = time_workload("c2", K, Wm, ST, Ks, clock_s=CS, algo=dg.DG_ALGO_VALU_F32)
+            extras["c2_valu"] = _summary("c2", v, ["--algo", str(dg.DG_ALGO_VALU_F32)])
+            del v
+        for key in ("c1", "c4", "c5", "flat16"):
+            if key in (args.workload, args.secondary):
+                continue
+            r = time_workload(key, K, Wm, ST, Ks)
+            extras[key] = _summary(key, r)
+            del r
+        # the split-K batch with the caches flushed before every call: its
+        # 134 MB A fits the 256 MB Infinity Cache, so back-to-back calls
+        # read it from there, not from HBM
+        flush = Flusher()
+        r = time_workload("c5", K, Wm, flush=flush)
+        extras["c5_cold"] = _summary("c5", r)
+        extras["c5_cold"]["note"] = ("512 MiB written between calls (outside the timed "
+                                     "event pairs): operands come from HBM")
+        del r, flush
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -472,8 +749,12 @@ def main():
         "frac_of_published_peak": main_r["tflops"] * 1e12 / published,
         "published_peak_tflops": published / 1e12,
         "roofline": roof,
+        "window": main_window,
+        "sustained": main_sus,
+        "clock_mhz": main_r.get("clock_mhz"),
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "extras": extras,
         "library_version": dg.dg_version(),
     }
     print(json.dumps(line), flush=True)

@@ -10,11 +10,15 @@ Verification).
 MI355X peaks (AMD's published figures, dense, no sparsity):
   - bf16 and fp16 MFMA 2516.6 TFLOP/s, fp32 (vector and matrix) 157.3 TFLOP/s,
     HBM3E 8 TB/s; 256 compute units at 2.4 GHz.
-  - FP32 vector without packed-FP32 instructions: each of the 4 SIMDs of a
-    CU retires 16 fp32 FMA lanes per clock, i.e. 64 FMA = 128 flop per clock
-    per CU: 256 * 128 * 2.4e9 = 78.6 TFLOP/s.  The library is built with
-    packed-FP32 instructions disabled, so this is the ceiling of its
-    vector-FMA SGEMM.
+  - FP32 vector: 256 flop per clock per CU (256 * 256 * 2.4e9 = 157.3
+    TFLOP/s), reached on gfx950 by the two-operand accumulate form of the
+    fp32 FMA (v_fmac_f32), which issues at twice the rate of the
+    three-operand v_fma_f32 without any packed-FP32 instruction.  Measured
+    with a loop of independent FMA chains on every CU, with the shader
+    clock of each dispatch from GRBM_GUI_ACTIVE: v_fmac_f32 ~234 flop/clk/CU
+    at 2.17 GHz, v_fma_f32 ~124 at 2.39 GHz, v_fma_f64 ~119 at 2.30 GHz
+    (the fp64 vector peak, 128 flop/clk/CU, 78.6 TFLOP/s).  The vector-FMA
+    SGEMM, whose inner loop is v_fmac_f32, is held to the 157.3 figure.
 """
 from __future__ import annotations
 
@@ -23,7 +27,8 @@ CLOCK_HZ = 2.4e9
 PEAK_BF16_MFMA = 2516.6e12          # 256 CU * 4096 flop/clk * 2.4 GHz
 PEAK_F16_MFMA = 2516.6e12           # same rate for fp16 inputs
 PEAK_F32 = 157.3e12                 # published fp32 vector / matrix peak
-PEAK_F32_VALU_UNPACKED = N_CU * 128 * CLOCK_HZ   # 78.64e12
+PEAK_F32_VALU = N_CU * 256 * CLOCK_HZ            # 157.29e12, fp32 vector (v_fmac_f32)
+PEAK_F64_VALU = N_CU * 128 * CLOCK_HZ            # 78.64e12
 PEAK_HBM = 8.0e12                   # bytes / s
 
 _ELEM = {"f32": 4, "bf16": 2, "f16": 2}

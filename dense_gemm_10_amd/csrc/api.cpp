@@ -219,7 +219,8 @@ const TileConfig *forced_tile(const TileConfig *table, int n)
 
 // Offline-tuned plans, generated by dense_gemm_10_amd/tune.py from timed
 // sweeps on an MI355X over every tile configuration of a family and both
-// schedules ("GEMM Kernel Optimization", Autotuning: benchmark the
+// schedules ("GEMM Kernel Optimization", Autotune Configs, and "Skill:
+// Write a Triton GEMM Kernel", Required reasoning process step 7: time the
 // candidate configurations per problem size and keep the fastest; here the
 // sweep runs once, offline, and its winners are compiled in, so no call
 // ever benchmarks).  An exact (family, M, N, K, batch) match replaces the

@@ -109,8 +109,8 @@ __device__ __forceinline__ void dma_16(const void *base, uint32_t voff, uint32_t
 }
 
 // Cache policy of the tile loads.  The pages suggest evict-first for A and
-// evict-last for B ("GEMM Kernel Optimization", Memory Hierarchy
-// Optimization).  CDNA4's global loads carry no evict-last bit; their
+// evict-last for B ("Skill: Write a Triton GEMM Kernel", Kernel design
+// rules).  CDNA4's global loads carry no evict-last bit; their
 // evict-first counterpart is the non-temporal bit `nt` (streaming
 // replacement in the L2).  Building with -DDG_LOAD_POLICY_A=nt (or _B)
 // appends that bit to the A (or B) tile loads.  Off by default: measured on

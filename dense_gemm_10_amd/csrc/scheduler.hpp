@@ -14,13 +14,13 @@
 //      and the grouped order below stays local to one L2.
 //   2. Decode of the logical id L: t = L mod T, then split s, then batch b
 //      (tiles of one (b, s) are consecutive).
-//   3. Group-M swizzle of t, written as on "Skill: Write a Triton GEMM
-//      Kernel", Required reasoning process step 2 ("GEMM Kernel
-//      Optimization", L2 Cache Grouping): groups of G tile rows are walked
-//      column by column so that consecutive programs share A row panels and
-//      B column panels.  As printed there, the row inside the group is
-//      t mod group_rows (not the offset inside the group); that is also a
-//      bijection and is kept literally.
+//   3. Grouped tile order ("GEMM Kernel Optimization", L2 Cache Grouping;
+//      "Skill: Write a Triton GEMM Kernel", Required reasoning process
+//      step 2): the tile rows are cut into bands of G rows (the last band
+//      may be shorter), the bands are taken top to bottom, and inside a
+//      band the tiles are taken column by column, top to bottom within a
+//      column.  A run of consecutive programs then reuses the same few A
+//      row panels and B column panels instead of sweeping a whole tile row.
 #pragma once
 #include <stdint.h>
 
@@ -62,21 +62,24 @@ DG_HD inline int64_t xcd_remap(int64_t pid, int64_t P)
     return x * q + (x < r ? x : r) + pid / kNumXcd;
 }
 
-// Group-M swizzle of tile index t (0 <= t < num_pid_m * num_pid_n) into
-// (pid_m, pid_n); b and s are left 0.
+// Grouped order of tile index t (0 <= t < num_pid_m * num_pid_n) ->
+// (pid_m, pid_n); b and s are left 0.  Band `band` holds tile rows
+// [band * G, band * G + h) with h = min(G, rows left) and its h * num_pid_n
+// tiles; position o inside the band walks column o / h, row o mod h.
 DG_HD inline TileCoord decode_tile(int64_t t, const SchedArgs &a)
 {
-    const int64_t in_group = (int64_t)a.group_m * a.num_pid_n;
-    const int64_t group_id = t / in_group;
-    const int64_t first_m = group_id * a.group_m;
-    int64_t rows = a.num_pid_m - first_m;
-    if (rows > a.group_m)
-        rows = a.group_m;
+    const int64_t G = a.group_m;
+    const int64_t band_tiles = G * a.num_pid_n;      // tiles of a full band
+    const int64_t band = t / band_tiles;
+    const int64_t o = t - band * band_tiles;         // position inside the band
+    const int64_t row0 = band * G;
+    const int64_t left = a.num_pid_m - row0;
+    const int64_t h = left < G ? left : G;           // rows in this band
     TileCoord c;
     c.b = 0;
     c.s = 0;
-    c.pid_m = (int32_t)(first_m + t % rows);
-    c.pid_n = (int32_t)((t % in_group) / rows);
+    c.pid_m = (int32_t)(row0 + o % h);
+    c.pid_n = (int32_t)(o / h);
     return c;
 }
 

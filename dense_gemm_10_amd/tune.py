@@ -9,9 +9,10 @@ tail tile) and, where the output tiles alone fill less than a wave of the
 256 compute units, with 2 to 16 split-K slices,
 next to the library's own heuristic plan
 (timed with the table switched off, DG_TUNED=0).  This is the per-size
-benchmark-and-keep-the-fastest of "GEMM Kernel Optimization" (Autotuning)
-and of "Skill: Write a Triton GEMM Kernel" (Output format: autotune
-configurations keyed on M, N, K), done once, offline: the winners are
+benchmark-and-keep-the-fastest of "GEMM Kernel Optimization" (Autotune
+Configs) and of "Skill: Write a Triton GEMM Kernel" (Required reasoning
+process step 7: configurations over tile sizes and pipeline depth, keyed
+on M, N, K), done once, offline: the winners are
 written as C initialisers to csrc/tuned_table.inc, which the planner
 compiles in, and no call ever benchmarks.
 

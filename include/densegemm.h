@@ -189,7 +189,10 @@ int dg_version(void);
 const char *dg_status_string(dg_status s);
 
 /* Device bytes of workspace that dg_gemm would use for `d` (0 when the
- * chosen plan needs none).  With split_k == 0 and schedule == 0 this is the
+ * chosen plan needs none).  The workspace holds fp32 partial sums: of
+ * every K slice of a split-K plan, reduced in a separate pass ("Skill:
+ * Write a Triton GEMM Kernel", Kernel design rules, on split-K), or of the
+ * tail tiles' K slices of a stream-K plan.  With split_k == 0 and schedule == 0 this is the
  * size that lets the library pick split-K or Stream-K where they pay.  Returns INVALID_VALUE /
  * NOT_SUPPORTED for descriptors dg_gemm would reject. */
 dg_status dg_gemm_workspace_size(const dg_gemm_desc *d, size_t *bytes);
@@ -216,8 +219,9 @@ dg_status dg_gemm(const dg_gemm_desc *d, const void *A, const void *B, void *C,
  * columns.  "tuned=1" marks a plan taken from the library's
  * offline-tuned table: for the exact (kernel family, M, N, K, batch) of a
  * shape swept on an MI355X, the tile and schedule that measured fastest
- * replace the heuristic choice ("GEMM Kernel Optimization", Autotuning,
- * with the benchmarking done once, offline). */
+ * replace the heuristic choice ("GEMM Kernel Optimization", Autotune
+ * Configs; "Skill: Write a Triton GEMM Kernel", Required reasoning process
+ * step 7; with the benchmarking done once, offline). */
 dg_status dg_gemm_describe(const dg_gemm_desc *d, size_t workspace_bytes, char *buf,
                            size_t len);
 

@@ -63,4 +63,6 @@ def test_workload_accounting():
 def test_mi355x_peaks():
     assert acc.PEAK_BF16_MFMA == pytest.approx(256 * 4096 * 2.4e9, rel=1e-4)
     assert acc.PEAK_F32 == pytest.approx(256 * 256 * 2.4e9, rel=1e-3)
-    assert acc.PEAK_F32_VALU_UNPACKED == pytest.approx(acc.PEAK_F32 / 2, rel=1e-3)
+    # the vector-FMA peak from unit counts and clock is the published fp32 figure
+    assert acc.PEAK_F32_VALU == pytest.approx(acc.PEAK_F32, rel=1e-3)
+    assert acc.PEAK_F64_VALU == pytest.approx(78.6e12, rel=1e-3)

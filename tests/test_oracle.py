@@ -324,6 +324,56 @@ def test_p8_gelu_tanh_close_to_erf_form():
     assert d > 1e-6     # and it is a different function
 
 
+# The tanh form is x (1 + tanh y) / 2 with y = sqrt(2/pi) (x + 0.044715 x^3).
+# Where tanh y takes a chosen value tau, it equals x (1 + tau) / 2 exactly;
+# y = atanh(tau) = ln((1 + tau) / (1 - tau)) / 2 and the x with that y is the
+# root of an increasing cubic, found here by bisection in 50-digit decimals.
+# A slip in either constant moves tanh y off tau by about 1e-6 (0.0447 for
+# 0.044715) or 1e-3 (0.8 for sqrt(2/pi)) and fails the 1e-13 check.
+def _x_where_tanh_is(tau):
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    y = ((1 + Decimal(tau)) / (1 - Decimal(tau))).ln() / 2
+    # sqrt(2/pi) to 40 digits from pi = 3.14159265358979323846264338327950288419
+    pi = Decimal("3.14159265358979323846264338327950288419")
+    s = (Decimal(2) / pi).sqrt()
+    c = Decimal("0.044715")
+    lo, hi = Decimal(-10), Decimal(10)
+    for _ in range(200):
+        mid = (lo + hi) / 2
+        if s * (mid + c * mid ** 3) < y:
+            lo = mid
+        else:
+            hi = mid
+    return float((lo + hi) / 2)
+
+
+@pytest.mark.parametrize("tau", [0.5, -0.5, 0.8, -0.8, 0.25, 0.95])
+def test_p8_gelu_tanh_where_tanh_is_known(tau):
+    x = _x_where_tanh_is(tau)
+    want = x * (1.0 + tau) / 2.0          # 0.75 x at tau = 1/2
+    got = oracle.act(x, "gelu_tanh")
+    assert abs(got - want) <= 1e-13 * max(1.0, abs(x)), (tau, x, got, want)
+
+
+def test_p8_gelu_tanh_high_precision_points():
+    """Four points evaluated from the definition in 50-digit decimal
+    arithmetic, tanh through exp (tanh y = (e^2y - 1) / (e^2y + 1)), held to
+    the oracle within 1e-14 relative."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    pi = Decimal("3.14159265358979323846264338327950288419")
+    s = (Decimal(2) / pi).sqrt()
+    c = Decimal("0.044715")
+    for xs in ("-2.75", "-0.3", "0.7", "1.9"):
+        x = Decimal(xs)
+        y = s * (x + c * x ** 3)
+        e = (2 * y).exp()
+        want = x * (1 + (e - 1) / (e + 1)) / 2
+        got = oracle.act(float(x), "gelu_tanh")
+        assert abs(Decimal(got) - want) <= Decimal("1e-14") * abs(want), (xs, got, want)
+
+
 # ---------------------------------------------------------------------------
 # P9: bf16 round to nearest even
 # ---------------------------------------------------------------------------

@@ -3,9 +3,13 @@ evaluated on the host by the same code the kernels run (dg_schedule_map).
 
 The map must be a bijection onto every (b, s, pid_m, pid_n) with ceil-div
 tile counts ("Skill: Write a Triton GEMM Kernel", Correctness requirements
-and Common failure modes), and without the XCD remap it must equal the
-group-M swizzle written as on that page (Required reasoning process,
-step 2), re-implemented independently below."""
+and Common failure modes).  Without the XCD remap it must be the grouped
+order of "GEMM Kernel Optimization", L2 Cache Grouping: bands of G tile
+rows, each walked column by column.  That order is checked against a list
+built by plain enumeration (nested loops over bands, columns and rows, no
+index arithmetic shared with the library), and its purpose, fewer distinct
+A and B panels per run of consecutive programs than row-major order, is
+checked directly."""
 import itertools
 
 import numpy as np
@@ -14,15 +18,17 @@ import pytest
 import dense_gemm_10_amd as dg
 
 
-def _page_swizzle(pid, num_pid_m, num_pid_n, group):
-    """Group-M tile order, step by step as on the Skill page."""
-    num_pid_in_group = group * num_pid_n
-    group_id = pid // num_pid_in_group
-    first_pid_m = group_id * group
-    group_size_m = min(num_pid_m - first_pid_m, group)
-    pid_m = first_pid_m + (pid % group_size_m)
-    pid_n = (pid % num_pid_in_group) // group_size_m
-    return pid_m, pid_n
+def _grouped_order(num_pid_m, num_pid_n, group):
+    """The grouped tile order as an explicit list of (tile row, tile column),
+    built by enumeration: bands of `group` tile rows from the top, each band
+    column by column from the left, each column top to bottom."""
+    order = []
+    for first in range(0, num_pid_m, group):
+        rows = range(first, min(first + group, num_pid_m))
+        for col in range(num_pid_n):
+            for row in rows:
+                order.append((row, col))
+    return order
 
 
 def _is_bijection(m, batch, splits, npm, npn):
@@ -63,11 +69,37 @@ def test_real_grids_use_ceil_div(M, N, bm, bn):
         assert (m[:, 2] == npm - 1).any() and (m[:, 3] == npn - 1).any()
 
 
-def test_without_remap_equals_page_formula():
-    for npm, npn, g in itertools.product([1, 2, 7, 16, 33], [1, 3, 16, 17], [1, 4, 8, 16]):
+def test_without_remap_equals_enumerated_order():
+    for npm, npn, g in itertools.product([1, 2, 7, 16, 33], [1, 3, 16, 17], [1, 3, 4, 8, 16]):
         m = dg.dg_schedule_map(npm, npn, 1, 1, 1, 1, g, -1)
-        for pid in range(npm * npn):
-            assert tuple(m[pid, 2:]) == _page_swizzle(pid, npm, npn, g)
+        want = _grouped_order(npm, npn, g)
+        assert [tuple(r) for r in m[:, 2:].tolist()] == want, (npm, npn, g)
+
+
+def _panels_per_window(coords, window):
+    """Mean number of distinct A row panels plus B column panels over the
+    aligned runs of `window` consecutive programs (the contiguous runs the
+    XCD remap hands to one L2)."""
+    counts = []
+    for s in range(0, len(coords), window):
+        run = coords[s:s + window]
+        counts.append(len({r for r, _ in run}) + len({c for _, c in run}))
+    return sum(counts) / len(counts)
+
+
+@pytest.mark.parametrize("npm,npn,g,window", [(16, 16, 8, 32), (32, 32, 8, 64), (17, 17, 8, 32),
+                                              (16, 16, 4, 16)])
+def test_grouping_reuses_panels(npm, npn, g, window):
+    """A window of consecutive programs the size of one wave share of an
+    L2 (e.g. 32 tiles of one XCD) loads fewer panels in grouped order than
+    in row-major order, and every band of the grouped order touches only
+    its own g tile rows."""
+    grouped = [tuple(r) for r in dg.dg_schedule_map(npm, npn, 1, 1, 1, 1, g, -1)[:, 2:].tolist()]
+    rowmajor = [tuple(r) for r in dg.dg_schedule_map(npm, npn, 1, 1, 1, 1, 1, -1)[:, 2:].tolist()]
+    assert _panels_per_window(grouped, window) < _panels_per_window(rowmajor, window)
+    for band in range(0, npm, g):
+        lo, hi = band * npn, min(band + g, npm) * npn
+        assert {r for r, _ in grouped[lo:hi]} == set(range(band, min(band + g, npm)))
 
 
 def test_group_one_is_row_major():
