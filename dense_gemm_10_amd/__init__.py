@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the GEMM runs in the HIP kernels
 behind the C ABI declared in include/densegemm.h.  The functions below carry
 the ABI's names (dg_gemm, dg_gemm_workspace_size, dg_gemm_describe,
-dg_status_string, dg_version, dg_schedule_map).  ``gemm()`` is a
+dg_status_string, dg_version, dg_schedule_map, dg_gemm_noalloc).  ``gemm()`` is a
 convenience wrapper for torch tensors; torch is used for device memory and
 streams only.
 
@@ -22,7 +22,7 @@ __all__ = [
     "DG_ALGO_AUTO", "DG_ALGO_GENERIC", "DG_ALGO_VALU_F32", "DG_ALGO_MFMA_BF16",
     "DG_ALGO_MFMA_F32", "DG_ALGO_MFMA_F16", "DgGemmDesc", "DgError", "make_desc", "dg_version",
     "dg_status_string", "dg_gemm_workspace_size", "dg_gemm", "dg_gemm_describe",
-    "dg_schedule_map", "gemm", "library_path",
+    "dg_schedule_map", "dg_gemm_noalloc", "DG_NOALLOC_SCRATCH_BYTES", "gemm", "library_path",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,6 +43,7 @@ DG_ACT_NONE, DG_ACT_GELU_ERF, DG_ACT_GELU_TANH = 0, 1, 2
 (DG_ALGO_AUTO, DG_ALGO_GENERIC, DG_ALGO_VALU_F32, DG_ALGO_MFMA_BF16, DG_ALGO_MFMA_F32,
  DG_ALGO_MFMA_F16) = range(6)
 DG_SCHED_AUTO, DG_SCHED_DATA_PARALLEL, DG_SCHED_STREAM_K = range(3)
+DG_NOALLOC_SCRATCH_BYTES = 64 << 20     # per-GPU scratch of dg_gemm_noalloc
 
 _DTYPE = {"f32": DG_F32, "bf16": DG_BF16, "f16": DG_F16}
 _ORDER = {"row": DG_ROW_MAJOR, "col": DG_COL_MAJOR}
@@ -101,6 +102,8 @@ def _load():
             lib.dg_gemm_workspace_size.restype = ctypes.c_int
             lib.dg_gemm.argtypes = [D, vp, vp, vp, vp, ctypes.c_size_t, vp]
             lib.dg_gemm.restype = ctypes.c_int
+            lib.dg_gemm_noalloc.argtypes = [D, vp, vp, vp, vp]
+            lib.dg_gemm_noalloc.restype = ctypes.c_int
             lib.dg_gemm_describe.argtypes = [D, ctypes.c_size_t, ctypes.c_char_p, ctypes.c_size_t]
             lib.dg_gemm_describe.restype = ctypes.c_int
             lib.dg_schedule_map.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -178,6 +181,15 @@ def dg_gemm(desc, A, B, C, workspace=None, workspace_bytes=0, stream=None, check
     st = _load().dg_gemm(ctypes.byref(desc), A, B, C, workspace, int(workspace_bytes), stream)
     if check and st != DG_SUCCESS:
         raise DgError(st, "dg_gemm")
+    return st
+
+
+def dg_gemm_noalloc(desc, A, B, C, stream=None, check=True):
+    """Enqueue the GEMM with the library's own per-GPU scratch as workspace
+    (no allocation).  Same arguments as dg_gemm minus the workspace."""
+    st = _load().dg_gemm_noalloc(ctypes.byref(desc), A, B, C, stream)
+    if check and st != DG_SUCCESS:
+        raise DgError(st, "dg_gemm_noalloc")
     return st
 
 

@@ -14,6 +14,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/densegemm.h"
 #include "launch.hpp"
 
@@ -618,6 +620,74 @@ void fill_args(const dg_gemm_desc *d, const Plan &p, const void *A, const void *
     g->sk_parts = p.sk.tail_tiles > 0 ? (float *)ws : nullptr;
 }
 
+// Enqueue the kernels of a validated call plan on `s`; `ws` is workspace
+// of at least cp.plan.workspace_bytes (or null when the plan needs none).
+dg_status enqueue(const dg_gemm_desc *d, const CallPlan &cp, const void *A, const void *B,
+                  void *C, void *ws, hipStream_t s)
+{
+    const Plan &p = cp.plan;
+    GemmArgs g;
+    fill_args(&cp.main, p, A, B, C, ws, &g);
+    hipError_t err = hipSuccess;
+    switch (p.kernel) {
+    case KERNEL_GENERIC: err = launch_generic(g, p, s); break;
+    case KERNEL_VALU_F32: err = launch_valu_f32(g, p, s); break;
+    case KERNEL_MFMA_BF16:
+    case KERNEL_MFMA_F16: err = launch_mfma16(g, p, s); break;
+    case KERNEL_MFMA_F32: err = launch_mfma_f32(g, p, s); break;
+    default: return DG_ERROR_NOT_SUPPORTED;
+    }
+    if (err != hipSuccess)
+        return DG_ERROR_LAUNCH;
+    if (p.splits > 1) {
+        err = launch_splitk_reduce(g, p, s);
+        if (err != hipSuccess)
+            return DG_ERROR_LAUNCH;
+    }
+    if (p.sk.tail_tiles > 0) {
+        err = launch_streamk_fixup(g, p, s);
+        if (err != hipSuccess)
+            return DG_ERROR_LAUNCH;
+    }
+    if (cp.nrem > 0) {
+        GemmArgs gs;
+        fill_args(d, p, A, B, C, nullptr, &gs);
+        err = launch_sliver(gs, cp.main.N, cp.nrem, s);
+        if (err != hipSuccess)
+            return DG_ERROR_LAUNCH;
+    }
+    return DG_SUCCESS;
+}
+
+// Workspace of dg_gemm_noalloc: one array per GPU, part of the library's
+// device code, so it exists from the library's load until the process
+// ends and no call allocates.  Host code never uses the array's name as
+// an address (on the host it names a stand-in, not device memory): each
+// device's own copy is looked up once with hipGetSymbolAddress, with that
+// device current, and that pointer is what the kernels receive.
+constexpr size_t kScratchBytes = DG_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// The scratch array of the current device, or null if the runtime fails.
+void *scratch_on_current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 const char *kernel_name(Kernel k)
 {
     switch (k) {
@@ -720,46 +790,44 @@ dg_status dg_gemm(const dg_gemm_desc *d, const void *A, const void *B, void *C, 
     st = make_call_plan(d, A, B, workspace ? workspace_bytes : 0, true, &cp);
     if (st != DG_SUCCESS)
         return st;
-    const Plan &p = cp.plan;
-    if (p.workspace_bytes > 0) {
-        if (!workspace || workspace_bytes < p.workspace_bytes)
+    if (cp.plan.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < cp.plan.workspace_bytes)
             return DG_ERROR_INSUFFICIENT_WORKSPACE;
         if (!aligned_to(workspace, 16) ||
-            ranges_overlap(workspace, (int64_t)p.workspace_bytes, C, e.c_bytes))
+            ranges_overlap(workspace, (int64_t)cp.plan.workspace_bytes, C, e.c_bytes))
             return DG_ERROR_INVALID_VALUE;
     }
-    GemmArgs g;
-    fill_args(&cp.main, p, A, B, C, workspace, &g);
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t err = hipSuccess;
-    switch (p.kernel) {
-    case KERNEL_GENERIC: err = launch_generic(g, p, s); break;
-    case KERNEL_VALU_F32: err = launch_valu_f32(g, p, s); break;
-    case KERNEL_MFMA_BF16:
-    case KERNEL_MFMA_F16: err = launch_mfma16(g, p, s); break;
-    case KERNEL_MFMA_F32: err = launch_mfma_f32(g, p, s); break;
-    default: return DG_ERROR_NOT_SUPPORTED;
-    }
-    if (err != hipSuccess)
-        return DG_ERROR_LAUNCH;
-    if (p.splits > 1) {
-        err = launch_splitk_reduce(g, p, s);
-        if (err != hipSuccess)
+    return enqueue(d, cp, A, B, C, workspace, (hipStream_t)stream);
+}
+
+dg_status dg_gemm_noalloc(const dg_gemm_desc *d, const void *A, const void *B, void *C,
+                          void *stream)
+{
+    Extents e;
+    dg_status st = validate_desc(d, &e);
+    if (st != DG_SUCCESS)
+        return st;
+    st = validate_ptrs(d, e, A, B, C);
+    if (st != DG_SUCCESS)
+        return st;
+    if (is_noop(d))
+        return DG_SUCCESS;
+    // The plan sees the scratch array as the caller's workspace: the
+    // automatic choice never asks for more; a forced split-K or stream-K
+    // plan that would is refused before any runtime call.
+    CallPlan cp;
+    st = make_call_plan(d, A, B, kScratchBytes, true, &cp);
+    if (st != DG_SUCCESS)
+        return st;
+    void *ws = nullptr;
+    if (cp.plan.workspace_bytes > 0) {
+        if (cp.plan.workspace_bytes > kScratchBytes)
+            return DG_ERROR_INSUFFICIENT_WORKSPACE;
+        ws = scratch_on_current_device();
+        if (!ws)
             return DG_ERROR_LAUNCH;
     }
-    if (p.sk.tail_tiles > 0) {
-        err = launch_streamk_fixup(g, p, s);
-        if (err != hipSuccess)
-            return DG_ERROR_LAUNCH;
-    }
-    if (cp.nrem > 0) {
-        GemmArgs gs;
-        fill_args(d, p, A, B, C, nullptr, &gs);
-        err = launch_sliver(gs, cp.main.N, cp.nrem, s);
-        if (err != hipSuccess)
-            return DG_ERROR_LAUNCH;
-    }
-    return DG_SUCCESS;
+    return enqueue(d, cp, A, B, C, ws, (hipStream_t)stream);
 }
 
 dg_status dg_schedule_map(int64_t M, int64_t N, int64_t batch, int32_t split_k, int32_t bm,

@@ -29,8 +29,11 @@
  *     before later work on the same stream.
  *   - Errors: return codes only.  Every argument is validated on the host
  *     before anything is enqueued, so any status other than DG_SUCCESS and
- *     DG_ERROR_LAUNCH means nothing was enqueued.  The library keeps no
- *     mutable global state; calls are thread-safe and reentrant.
+ *     DG_ERROR_LAUNCH means nothing was enqueued.  The only mutable global
+ *     state is the per-device address of dg_gemm_noalloc's scratch array,
+ *     looked up once under a lock; calls are thread-safe and reentrant
+ *     (dg_gemm_noalloc calls that overlap on one GPU share its scratch; see
+ *     there).
  *   - Determinism: results are bitwise reproducible run to run for a given
  *     descriptor, including split-K (partials are reduced in a fixed order,
  *     never with atomics).
@@ -210,6 +213,31 @@ dg_status dg_gemm_workspace_size(const dg_gemm_desc *d, size_t *bytes);
  * Returns DG_SUCCESS once the work is enqueued. */
 dg_status dg_gemm(const dg_gemm_desc *d, const void *A, const void *B, void *C,
                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Size in bytes of the per-GPU scratch array of dg_gemm_noalloc. */
+#define DG_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* dg_gemm for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same operation, arguments (minus the workspace), validation, plans and
+ * results as dg_gemm given DG_NOALLOC_SCRATCH_BYTES of workspace, except
+ * that split-K and stream-K partials go to a scratch array of that size
+ * that is part of the library's device code: each GPU the library runs on
+ * holds one copy from the library's load until the process ends, and no
+ * call allocates or frees anything (no hipMalloc / hipFree, no allocating
+ * library routine).  The first call on a device looks up that device's copy
+ * (hipGetSymbolAddress, with the device current); later calls reuse it.
+ *   - The automatic choice never plans more than DG_NOALLOC_SCRATCH_BYTES
+ *     of workspace.  A forced split_k or STREAM_K schedule whose workspace
+ *     (see dg_gemm_workspace_size) exceeds it returns
+ *     DG_ERROR_INSUFFICIENT_WORKSPACE before anything is enqueued.
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's partials; nothing in it needs to start at zero.  Calls whose
+ *     work overlaps in time on one GPU (other streams, other host threads)
+ *     race on it: order them on one stream or serialise them.
+ *   - DG_ERROR_LAUNCH also covers a failed device or symbol lookup. */
+dg_status dg_gemm_noalloc(const dg_gemm_desc *d, const void *A, const void *B, void *C,
+                          void *stream);
 
 /* Write a one-line, NUL-terminated description of the plan dg_gemm would
  * run for `d` (kernel, tile, split, grid, workspace) into buf[len].  Pass

@@ -166,6 +166,21 @@ def test_forced_split_needs_workspace():
     assert _gemm_status(d, ws=PC, ws_bytes=need) == dg.DG_ERROR_INVALID_VALUE
 
 
+def test_noalloc_refuses_forced_plans_beyond_its_scratch():
+    """dg_gemm_noalloc plans against DG_NOALLOC_SCRATCH_BYTES and refuses a
+    forced split-K whose workspace exceeds it, on the host, before any
+    runtime call (fake, far-apart addresses: nothing is dereferenced)."""
+    A, B, C = 1 << 40, 2 << 40, 3 << 40
+    d = _desc(M=4096, N=4096, K=4096, lda=4096, ldb=4096, ldc=4096, split_k=2)
+    assert dg.dg_gemm_workspace_size(d) > dg.DG_NOALLOC_SCRATCH_BYTES
+    assert dg.dg_gemm_noalloc(d, A, B, C, check=False) == dg.DG_ERROR_INSUFFICIENT_WORKSPACE
+    # validation errors come first, as for dg_gemm
+    assert dg.dg_gemm_noalloc(d, A, B, None, check=False) == dg.DG_ERROR_INVALID_VALUE
+    bad = _desc(M=-1)
+    assert dg.dg_gemm_noalloc(bad, A, B, C, check=False) == dg.DG_ERROR_INVALID_VALUE
+    assert dg.dg_gemm_noalloc(_desc(M=0), None, None, None, check=False) == dg.DG_SUCCESS
+
+
 def _desc_for(p, **kw):
     f = W.desc_fields(p)
     f.update(kw)
