@@ -189,14 +189,22 @@ bool valu_eligible(const dg_gemm_desc *d, const void *A, const void *B)
            strides_aligned(d, 4);
 }
 
-// bf16 or fp16 (`type`) matrix-core kernel
+// bf16 or fp16 (`type`) matrix-core kernel, any order of A and B
 bool mfma16_eligible(const dg_gemm_desc *d, int32_t type, const void *A, const void *B)
 {
-    if (d->a_type != type || d->a_order != DG_ROW_MAJOR || d->b_order != DG_COL_MAJOR)
+    if (d->a_type != type)
         return false;
     // the kernel addresses a tile with 32-bit byte offsets: 256 rows * ld * 2 < 2^31
     return aligned_to(A, 16) && aligned_to(B, 16) && d->lda % 8 == 0 && d->ldb % 8 == 0 &&
            strides_aligned(d, 8) && d->lda < (1 << 22) && d->ldb < (1 << 22);
+}
+
+// A row-major and B column-major: both operands K-contiguous, the layout
+// every 16-bit tile configuration (and the tuned table) serves.  The other
+// three run on the two tiles of the automatic choice.
+bool k_contiguous(const dg_gemm_desc *d)
+{
+    return d->a_order == DG_ROW_MAJOR && d->b_order == DG_COL_MAJOR;
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -488,6 +496,26 @@ dg_status make_plan(const dg_gemm_desc *d, const void *A, const void *B, size_t 
     // wave instead (automatic choice, workspace given), the large tile with
     // its better flop-per-byte ratio wins: 4352 x 4352 x 8192 (bf16) ran
     // 295 us that way against 415 us on 128 x 128 tiles.
+    // An M- or N-contiguous 16-bit operand: only the two tiles of the
+    // automatic choice have that variant, and the tuned table was swept on
+    // K-contiguous operands, so neither it nor a forced tile applies.
+    if (table16 && !k_contiguous(d)) {
+        const TileConfig &t256 = table16[0], &t128 = table16[1];
+        p.tile = (d->K <= 64 || p.tile.bm != t256.bm || p.tile.bn != t256.bn) ? t128 : t256;
+        if (keep)
+            p.tile = keep->bm == t256.bm && keep->bn == t256.bn ? t256 : t128;
+        Plan done;
+        if (p.tile.bm != t256.bm) {
+            Plan big = p;
+            big.tile = t256;
+            if (finish_plan(d, big, ws_avail, ws_known, 0, 0, &done) == DG_SUCCESS &&
+                done.sk.tail_tiles > 0 && !keep) {
+                *plan = done;
+                return DG_SUCCESS;
+            }
+        }
+        return finish_plan(d, p, ws_avail, ws_known, 0, 0, plan);
+    }
     const TunedEntry *tuned = nullptr;
     TunedEntry forced;
     if (table && forced_plan(table, ntab, p.kernel, &forced))

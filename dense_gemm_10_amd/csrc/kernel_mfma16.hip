@@ -11,9 +11,13 @@
 // registers, 32 x 32 x 16 MFMA fragments).  The multi-stage ring below is
 // the double buffering of that page's section 2.8 taken further.
 //
-// Operands: A row-major (M x K) and B column-major (K x N), i.e. both with
-// K contiguous, which is the order an MFMA lane consumes: lane l supplies 8
-// consecutive k of row (l mod 32) of A and of column (l mod 32) of B.
+// Operands: an MFMA lane consumes 8 consecutive k of row (l mod 32) of A
+// and of column (l mod 32) of B.  A row-major (M x K) and B column-major
+// (K x N) have K contiguous and are staged as rows of K (below); a
+// column-major A or row-major B (M or N contiguous, the orders of "Skill:
+// Write a Triton GEMM Kernel", Inputs the agent should gather first, item 3)
+// is staged as rows of M or N and transposed by the LDS reads (see
+// mfma16_tile), so every layout runs on the matrix cores.
 //
 // Data path:
 //   global -> LDS: direct DMA (global_load_lds_dwordx4): each instruction
@@ -47,10 +51,11 @@
 // M (or N) are clamped to the last row: the loads stay inside the matrix
 // and those rows only feed outputs that are never stored.
 //
-// Requirements checked on the host: bf16 or fp16 A (row-major) and B
-// (column-major), of one type; 16-byte aligned base pointers; lda, ldb and the batch strides
-// multiples of 8 elements; BM * lda and BN * ldb small enough for 32-bit
-// byte offsets inside a tile.
+// Requirements checked on the host: bf16 or fp16 A and B of one type;
+// 16-byte aligned base pointers; lda, ldb and the batch strides multiples
+// of 8 elements; BM * lda and BN * ldb (or BK * lda, BK * ldb) small enough
+// for 32-bit byte offsets inside a tile; an M- or N-contiguous operand only
+// on the 256 x 256 and 128 x 128 tiles.
 #include "epilogue.hpp"
 #include "launch.hpp"
 
@@ -202,10 +207,76 @@ constexpr int mfma16_per_cu(int BM, int BN, int NS, int BK)
     return by_lds < by_regs ? by_lds : by_regs;
 }
 
+// Slot of logical 16-byte chunk c in k-row `k` of an operand staged with its
+// M (or N) dimension contiguous: rows sit 64 bytes apart modulo the 256
+// bytes of LDS banks, so the four k-rows one transposing read touches get
+// four disjoint quarters of the banks.
+__device__ __forceinline__ int mn_slot(int c, int k)
+{
+    return c ^ (4 * (k & 3));
+}
+
+// 8 16-bit elements at columns col .. col+7 of one row of an operand whose
+// M (or N) dimension is contiguous, zero at columns >= ext (the M or N edge
+// of the tile).  A chunk wholly inside is one 16-byte load; the chunk that
+// straddles ext is read element by element with the index clamped to
+// ext - 1, so no load leaves the row's valid part.
+__device__ __forceinline__ uint4 load_chunk_cols(const uint16_t *row, int64_t col, int64_t ext)
+{
+    if (col + 8 <= ext)
+        return *(const uint4 *)(row + col);
+    if (col >= ext)
+        return make_uint4(0u, 0u, 0u, 0u);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int64_t c = col + j;
+        const uint32_t v = row[c < ext ? c : ext - 1];
+        w[j / 2] |= (c < ext ? v : 0u) << (16 * (j % 2));
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+
+// Fragment of an operand staged M- (or N-) contiguous: the 8 consecutive k
+// of one row (column of B) that MFMA lane l consumes, gathered by two
+// transposing LDS reads (ds_read_b64_tr_b16).  Within each group of 16
+// lanes that instruction returns to lane i the (i mod 4)-th element of the
+// 8-byte pieces addressed by lanes 4r + i / 4 of the group, r = 0 .. 3
+// (measured on gfx950).  So lane 4r + q of group g addresses k-row
+// kbase + r, columns 16 (g mod 2) + 4q .. +3 of the fragment, and lane
+// l = 16g + i receives k-rows kbase .. kbase + 3 of column 16 (g mod 2) + i
+// = l mod 32; kbase = 8 (l / 32) for the first read and 4 more for the
+// second.  `addr0` is the lane's byte address for the first read; the
+// second is 4 k-rows further.
+template <typename frag_t, int ROW_BYTES>
+__device__ __forceinline__ frag_t tr_fragment(uint32_t addr0)
+{
+    typedef __attribute__((address_space(3))) s16x4_t *lds_s4;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(uintptr_t)addr0);
+    const s16x4_t hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(uintptr_t)(addr0 + 4 * ROW_BYTES));
+    const s16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(frag_t, both);
+}
+
 // One output tile (or, for stream-K, one K range of it): K loop over
 // [kb, ke) and the epilogue, or the raw fp32 accumulators written to `part`
 // (a BM x BN row-major slot) when `part` is not null.
-template <int T, int BM, int BN, int WM, int WN, int kStages, int MBK>
+//
+// AT / BT: A is stored M-contiguous (column-major) / B is stored
+// N-contiguous (row-major).  Such an operand is staged as MBK k-rows of BM
+// (BN) elements, loaded by the same DMA (whole 16-byte chunks along M or
+// N, slots placed by mn_slot), and read into MFMA fragments by transposing
+// LDS reads; the K-contiguous operands keep rows of K as above.  Columns
+// past the M (N) edge are clamped to the last chunk that starts inside the
+// edge; where the edge cuts a chunk, that chunk reaches up to 7 elements
+// past the edge, inside the leading dimension for every k-row but the
+// matrix's last, so a K range that ends at K loads its last K tile through
+// registers with both masks.
+template <int T, int BM, int BN, int WM, int WN, int kStages, int MBK, bool AT, bool BT>
 __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int64_t kb,
                                             int64_t ke, float *part, uint4 *lds)
 {
@@ -219,14 +290,19 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
     constexpr int RPI = 64 / CPR;                // stage rows per DMA instruction
     constexpr int ROWS = BM + BN;                // stage rows: A rows, then B columns
     constexpr int GROUPS = ROWS / RPI;           // DMA instructions per stage
+    constexpr int A_GROUPS = BM / RPI;           // ... of A (the same count either layout)
     constexpr int LPW = GROUPS / NW;             // ... per wave
     constexpr int STAGE_SLOTS = ROWS * CPR;      // 16-byte slots per stage
     constexpr int D = kStages - 1;               // prefetch distance (tiles)
+    constexpr int A_CPK = BM / 8, B_CPK = BN / 8;   // chunks per k-row, M-/N-contiguous
     static_assert((D - 1) * LPW <= 63, "loads left in flight fit the vmcnt counter");
     static_assert(MBK == 32 || MBK == 64, "stage K width");
     static_assert(KS % 2 == 0, "fragment sets alternate per k-step");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be 32-aligned");
     static_assert(BM % RPI == 0 && BN % RPI == 0 && GROUPS % NW == 0, "DMA split");
+    static_assert((!AT || (A_CPK >= 16 && 64 % A_CPK == 0)) &&
+                  (!BT || (B_CPK >= 16 && 64 % B_CPK == 0)),
+                  "M-/N-contiguous staging needs 128 or 256 elements per k-row");
 
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)lds;
 
@@ -244,37 +320,70 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int wm = wave / WN, wn = wave % WN;
     const int64_t M = g.M, N = g.N, lda = g.lda, ldb = g.ldb;
-    const uint16_t *A_tile = (const uint16_t *)g.A + tc.b * g.sa + m0 * lda;
-    const uint16_t *B_tile = (const uint16_t *)g.B + tc.b * g.sb + n0 * ldb;
+    const int64_t a_ext = M - m0 < BM ? M - m0 : BM;   // valid rows of A / columns of B
+    const int64_t b_ext = N - n0 < BN ? N - n0 : BN;
+    // tile origin: row m0 (column n0) of a K-contiguous operand, column m0
+    // (n0) of k-row 0 of an M- (N-) contiguous one
+    const uint16_t *A_tile = (const uint16_t *)g.A + tc.b * g.sa + (AT ? m0 : m0 * lda);
+    const uint16_t *B_tile = (const uint16_t *)g.B + tc.b * g.sb + (BT ? n0 : n0 * ldb);
 
-    // This lane's DMA sources: group q = wave * LPW + i covers stage rows
-    // RPI q .. RPI q + RPI - 1 (A rows first, then B columns); lane l fills
-    // slot 64q + l = (row RPI q + l / CPR, physical chunk l % CPR), i.e.
-    // logical chunk (l % CPR) ^ key(row).  Byte offsets are relative to the
-    // tile's first row and K position; rows past the matrix are clamped.
+    // This lane's DMA sources.  Group q = wave * LPW + i fills slots
+    // 64q .. 64q + 63 of a stage (A's groups first, then B's); lane l fills
+    // slot 64q + l.  K-contiguous operand: stage row RPI q + l / CPR (a row
+    // of A or column of B, clamped to the matrix), physical chunk l % CPR,
+    // i.e. logical chunk (l % CPR) ^ key(row).  M-/N-contiguous operand:
+    // k-row (64 q' + l) / CPK of the operand's part (q' counted from the
+    // part's first group), slot (l % CPK), i.e. logical chunk mn_slot of
+    // it, at a column clamped as described above.  Byte offsets are
+    // relative to the tile origin at the stage's first k.
     uint32_t voff[LPW];
     bool from_a[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int q = wave * LPW + i;
-        const int srow = q * RPI + lane / CPR;                     // stage row
-        const int c = (lane % CPR) ^ swizzle_key<CPR>(srow);       // logical chunk
-        from_a[i] = q * RPI < BM;                     // per group, hence wave-uniform
-        int64_t r = from_a[i] ? srow : srow - BM;     // row inside the A / B tile
-        const int64_t lim = from_a[i] ? M - m0 : N - n0;
-        r = r < lim ? r : lim - 1;
-        voff[i] = (uint32_t)((r * (from_a[i] ? lda : ldb) + c * 8) * 2);
+        from_a[i] = q < A_GROUPS;                     // per group, hence wave-uniform
+        const bool mn = from_a[i] ? AT : BT;
+        if (mn) {
+            const int cpk = from_a[i] ? A_CPK : B_CPK;
+            const int qp = from_a[i] ? q : q - A_GROUPS;
+            const int k = (64 * qp + lane) / cpk;
+            const int c = mn_slot(lane % cpk, k);
+            const int64_t ext = from_a[i] ? a_ext : b_ext;
+            const int64_t cmax = 8 * ((ext - 1) / 8);    // last chunk starting inside
+            const int64_t col = 8 * c < cmax ? 8 * c : cmax;
+            voff[i] = (uint32_t)((k * (from_a[i] ? lda : ldb) + col) * 2);
+        } else {
+            const int srow = q * RPI + lane / CPR;                     // stage row
+            const int c = (lane % CPR) ^ swizzle_key<CPR>(srow);       // logical chunk
+            int64_t r = from_a[i] ? srow : srow - BM;     // row inside the A / B tile
+            const int64_t lim = from_a[i] ? a_ext : b_ext;
+            r = r < lim ? r : lim - 1;
+            voff[i] = (uint32_t)((r * (from_a[i] ? lda : ldb) + c * 8) * 2);
+        }
     }
 
-    // K position of virtual tile v: a partial tile (if any) comes first.
+    // K position of virtual tile v: a register-loaded tile (if any) comes
+    // first: the partial last K tile, or, where an M- or N-contiguous
+    // operand's edge cuts a chunk and this K range ends at K, the last full
+    // K tile.
     const int64_t klen = ke > kb ? ke - kb : 0;
-    const int64_t nfull = klen / MBK;
-    const bool tail = (klen % MBK) != 0;
+    const bool cut_edge = ke == g.K && ((AT && a_ext % 8 != 0) || (BT && b_ext % 8 != 0));
+    const bool tail = (klen % MBK) != 0 || (cut_edge && klen > 0);
+    const int64_t nfull = (klen % MBK) != 0 ? klen / MBK : (tail ? klen / MBK - 1 : klen / MBK);
     const int64_t ntiles = nfull + (tail ? 1 : 0);
     auto tile_k0 = [&](int64_t v) -> int64_t {
         if (tail)
             return v == 0 ? kb + nfull * MBK : kb + (v - 1) * MBK;
         return kb + v * MBK;
+    };
+
+    // Source of DMA group i at K position k0: the tile origin advanced by
+    // k0 along K (one element per k for a K-contiguous operand, one leading
+    // dimension for an M- or N-contiguous one).
+    auto group_base = [&](int i, int64_t k0) -> const uint16_t * {
+        if (from_a[i])
+            return A_tile + (AT ? k0 * lda : k0);
+        return B_tile + (BT ? k0 * ldb : k0);
     };
 
     // DMA instruction i (of LPW) of full tile v into its stage.
@@ -283,11 +392,10 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
         const uint32_t stage_addr = lds_base + (uint32_t)((v % kStages) * STAGE_SLOTS * 16);
         const int q = wave * LPW + i;
 #ifdef DG_LOAD_POLICY
-        dma_16_policy(from_a[i], uniform_ptr((from_a[i] ? A_tile : B_tile) + k0), voff[i],
+        dma_16_policy(from_a[i], uniform_ptr(group_base(i, k0)), voff[i],
                       stage_addr + (uint32_t)(q * 64 * 16));
 #else
-        dma_16(uniform_ptr((from_a[i] ? A_tile : B_tile) + k0), voff[i],
-               stage_addr + (uint32_t)(q * 64 * 16));
+        dma_16(uniform_ptr(group_base(i, k0)), voff[i], stage_addr + (uint32_t)(q * 64 * 16));
 #endif
     };
     auto issue_dma = [&](int64_t v) {
@@ -296,19 +404,34 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
             issue_dma_one(v, i);
     };
 
-    // The partial tile: same slots as the DMA, through registers, with the
-    // K mask.
+    // The register-loaded tile: same slots as the DMA, with the K mask (and
+    // the M / N mask on an M- or N-contiguous operand).
     auto load_tail = [&](int64_t v) {
         const int64_t k0 = tile_k0(v);
         uint4 *stage = lds + (v % kStages) * STAGE_SLOTS;
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             const int q = wave * LPW + i;
-            const int srow = q * RPI + lane / CPR;
-            const int c = (lane % CPR) ^ swizzle_key<CPR>(srow);
-            const uint16_t *rowp = (const uint16_t *)((const char *)(from_a[i] ? A_tile : B_tile) +
-                                                      voff[i]) - c * 8;
-            stage[q * 64 + lane] = load_chunk_tail(rowp, k0 + c * 8, ke);
+            const bool mn = from_a[i] ? AT : BT;
+            if (mn) {
+                const int cpk = from_a[i] ? A_CPK : B_CPK;
+                const int qp = from_a[i] ? q : q - A_GROUPS;
+                const int k = (64 * qp + lane) / cpk;
+                const int c = mn_slot(lane % cpk, k);
+                uint4 val = make_uint4(0u, 0u, 0u, 0u);
+                if (k0 + k < ke) {
+                    const int64_t ld = from_a[i] ? lda : ldb;
+                    const uint16_t *row = (from_a[i] ? A_tile : B_tile) + (k0 + k) * ld;
+                    val = load_chunk_cols(row, 8 * c, from_a[i] ? a_ext : b_ext);
+                }
+                stage[q * 64 + lane] = val;
+            } else {
+                const int srow = q * RPI + lane / CPR;
+                const int c = (lane % CPR) ^ swizzle_key<CPR>(srow);
+                const uint16_t *rowp = (const uint16_t *)((const char *)(from_a[i] ? A_tile : B_tile) +
+                                                          voff[i]) - c * 8;
+                stage[q * 64 + lane] = load_chunk_tail(rowp, k0 + c * 8, ke);
+            }
         }
     };
 
@@ -324,19 +447,28 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
     const int frag_row = lane & 31;       // row of A / column of B this lane feeds
     const int frag_half = lane >> 5;      // which 8 of the 16 k of one MFMA step
     const int swz = swizzle_key<CPR>(frag_row);   // key of every fragment row (period 16)
-
-    // Fragments of k-step ks (0 .. KS-1) of a stage.
-    auto load_frags = [&](int st, int ks, frag_t *af, frag_t *bf) {
-        const uint4 *as = lds + st * STAGE_SLOTS + (wm * TM + frag_row) * CPR;
-        const uint4 *bs = lds + st * STAGE_SLOTS + (BM + wn * TN + frag_row) * CPR;
-        const int c = (ks * 2 + frag_half) ^ swz;
+    // Transposing reads: lane 16g + 4r + q addresses k-row 8 (g / 2) + r of
+    // a k-step and columns 16 (g mod 2) + 4q .. + 3 of a fragment (see
+    // tr_fragment).  Byte offset of that piece inside an M-/N-contiguous
+    // part, k-step 0, first read, for the wave's fragment i (A) or j (B).
+    const int tr_g = lane >> 4, tr_r = (lane >> 2) & 3, tr_q = lane & 3;
+    const int tr_krow = 8 * (tr_g >> 1) + tr_r;
+    const int tr_chunk = 2 * (tr_g & 1) + (tr_q >> 1);    // chunk inside a 32-column fragment
+    uint32_t a_tr[AT ? FM : 1], b_tr[BT ? FN : 1];
+    if constexpr (AT) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            af[i] = __builtin_bit_cast(frag_t, as[i * 32 * CPR + c]);
+            a_tr[i] = (uint32_t)(tr_krow * BM * 2 +
+                                 16 * mn_slot((wm * TM + 32 * i) / 8 + tr_chunk, tr_krow) +
+                                 8 * (tr_q & 1));
+    }
+    if constexpr (BT) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            bf[j] = __builtin_bit_cast(frag_t, bs[j * 32 * CPR + c]);
-    };
+            b_tr[j] = (uint32_t)(BM * MBK * 2 + tr_krow * BN * 2 +
+                                 16 * mn_slot((wn * TN + 32 * j) / 8 + tr_chunk, tr_krow) +
+                                 8 * (tr_q & 1));
+    }
 
     auto mfma_step = [&](const frag_t *af, const frag_t *bf) {
 #pragma unroll
@@ -371,16 +503,26 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
     auto stage_body = [&](int st, bool dma, int64_t v_dma) {
         const uint4 *as = lds + st * STAGE_SLOTS + (wm * TM + frag_row) * CPR;
         const uint4 *bs = lds + st * STAGE_SLOTS + (BM + wn * TN + frag_row) * CPR;
+        const uint32_t st_addr = lds_base + (uint32_t)(st * STAGE_SLOTS * 16);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int cur = ks & 1, prev = cur ^ 1;
             const int c = (ks * 2 + frag_half) ^ swz;
 #pragma unroll
             for (int n = 0; n < FM * FN; ++n) {
-                if (n < FM)
-                    fa[cur][n] = __builtin_bit_cast(frag_t, as[n * 32 * CPR + c]);
-                else if (n < FM + FN)
-                    fb[cur][n - FM] = __builtin_bit_cast(frag_t, bs[(n - FM) * 32 * CPR + c]);
+                if (n < FM) {
+                    if constexpr (AT)
+                        fa[cur][n] = tr_fragment<frag_t, BM * 2>(st_addr + a_tr[n] +
+                                                                  16 * ks * BM * 2);
+                    else
+                        fa[cur][n] = __builtin_bit_cast(frag_t, as[n * 32 * CPR + c]);
+                } else if (n < FM + FN) {
+                    if constexpr (BT)
+                        fb[cur][n - FM] = tr_fragment<frag_t, BN * 2>(st_addr + b_tr[n - FM] +
+                                                                       16 * ks * BN * 2);
+                    else
+                        fb[cur][n - FM] = __builtin_bit_cast(frag_t, bs[(n - FM) * 32 * CPR + c]);
+                }
                 const int i = n / FN, j = n % FN;
                 acc[i][j] = mfma_32x32x16(fa[prev][i], fb[prev][j], acc[i][j]);
                 const int d = ks * FM * FN + n;
@@ -448,7 +590,7 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
 // Stream-K launches give programs [0, dp_tiles) one whole tile each and the
 // others one K slice of a tail tile, written as a raw fp32 partial that the
 // fix-up kernel adds up.
-template <int T, int BM, int BN, int WM, int WN, int kStages, int MBK>
+template <int T, int BM, int BN, int WM, int WN, int kStages, int MBK, bool AT, bool BT>
 __device__ __forceinline__ void mfma16_program(const GemmArgs &g, uint4 *lds)
 {
     const StreamK &sk = g.sk;
@@ -474,40 +616,64 @@ __device__ __forceinline__ void mfma16_program(const GemmArgs &g, uint4 *lds)
         ke = kb + sk.k_per_split < g.K ? kb + sk.k_per_split : g.K;
         part = g.sk_parts + (r * sk.tail_splits + slice) * (int64_t)(BM * BN);
     }
-    mfma16_tile<T, BM, BN, WM, WN, kStages, MBK>(g, tc, kb, ke, part, lds);
+    mfma16_tile<T, BM, BN, WM, WN, kStages, MBK, AT, BT>(g, tc, kb, ke, part, lds);
 }
 
-// One kernel name per element type, so that traces tell them apart.
-template <int BM, int BN, int WM, int WN, int kStages, int MBK>
+// One kernel name per element type, so that traces tell them apart.  AT /
+// BT: A stored M-contiguous (column-major) / B stored N-contiguous
+// (row-major).
+template <int BM, int BN, int WM, int WN, int kStages, int MBK, bool AT, bool BT>
 __global__ __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(mfma16_per_cu(BM, BN, kStages, MBK))))
 void gemm_mfma_bf16_kernel(GemmArgs g)
 {
     extern __shared__ uint4 lds[];
-    mfma16_program<DT_BF16, BM, BN, WM, WN, kStages, MBK>(g, lds);
+    mfma16_program<DT_BF16, BM, BN, WM, WN, kStages, MBK, AT, BT>(g, lds);
 }
 
-template <int BM, int BN, int WM, int WN, int kStages, int MBK>
+template <int BM, int BN, int WM, int WN, int kStages, int MBK, bool AT, bool BT>
 __global__ __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(mfma16_per_cu(BM, BN, kStages, MBK))))
 void gemm_mfma_f16_kernel(GemmArgs g)
 {
     extern __shared__ uint4 lds[];
-    mfma16_program<DT_F16, BM, BN, WM, WN, kStages, MBK>(g, lds);
+    mfma16_program<DT_F16, BM, BN, WM, WN, kStages, MBK, AT, BT>(g, lds);
 }
 
-template <int T, int BM, int BN, int WM, int WN, int NS, int BK>
-hipError_t launch_one(const GemmArgs &g, const Plan &p, hipStream_t stream)
+template <int T, int BM, int BN, int WM, int WN, int NS, int BK, bool AT, bool BT>
+hipError_t launch_layout(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
     const size_t lds_bytes = (size_t)mfma16_lds_bytes(BM, BN, NS, BK);
     const dim3 grid((unsigned)p.programs), block(64 * WM * WN);
     if constexpr (T == DT_F16)
-        hipLaunchKernelGGL((gemm_mfma_f16_kernel<BM, BN, WM, WN, NS, BK>), grid, block, lds_bytes,
-                           stream, g);
+        hipLaunchKernelGGL((gemm_mfma_f16_kernel<BM, BN, WM, WN, NS, BK, AT, BT>), grid, block,
+                           lds_bytes, stream, g);
     else
-        hipLaunchKernelGGL((gemm_mfma_bf16_kernel<BM, BN, WM, WN, NS, BK>), grid, block, lds_bytes,
-                           stream, g);
+        hipLaunchKernelGGL((gemm_mfma_bf16_kernel<BM, BN, WM, WN, NS, BK, AT, BT>), grid, block,
+                           lds_bytes, stream, g);
     return hipGetLastError();
+}
+
+// K-contiguous A and B (A row-major, B column-major) on any tile; the
+// other three layouts on the tiles of the automatic choice (the 256 x 256
+// and 128 x 128 tiles), which the planner restricts them to.
+template <int T, int BM, int BN, int WM, int WN, int NS, int BK>
+hipError_t launch_one(const GemmArgs &g, const Plan &p, hipStream_t stream)
+{
+    return launch_layout<T, BM, BN, WM, WN, NS, BK, false, false>(g, p, stream);
+}
+
+template <int T, int BM, int BN, int WM, int WN, int NS, int BK>
+hipError_t launch_any_layout(const GemmArgs &g, const Plan &p, hipStream_t stream)
+{
+    const bool at = g.a_col != 0, bt = g.b_col == 0;
+    if (at && bt)
+        return launch_layout<T, BM, BN, WM, WN, NS, BK, true, true>(g, p, stream);
+    if (at)
+        return launch_layout<T, BM, BN, WM, WN, NS, BK, true, false>(g, p, stream);
+    if (bt)
+        return launch_layout<T, BM, BN, WM, WN, NS, BK, false, true>(g, p, stream);
+    return launch_layout<T, BM, BN, WM, WN, NS, BK, false, false>(g, p, stream);
 }
 
 } // namespace
@@ -544,20 +710,23 @@ const int kNumMfmaF16Tiles = 2;
 
 hipError_t launch_mfma16(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
+    const bool k_contiguous = g.a_col == 0 && g.b_col != 0;
+    if (!k_contiguous && p.tile.variant != 1 && p.tile.variant != 5)
+        return hipErrorInvalidValue;      // the planner never asks for this
     if (g.ab_type == DT_F16) {
         switch (p.tile.variant) {
-        case 1: return launch_one<DT_F16, 128, 128, 2, 2, 4, 32>(g, p, stream);
-        case 5: return launch_one<DT_F16, 256, 256, 2, 2, 2, 64>(g, p, stream);
+        case 1: return launch_any_layout<DT_F16, 128, 128, 2, 2, 4, 32>(g, p, stream);
+        case 5: return launch_any_layout<DT_F16, 256, 256, 2, 2, 2, 64>(g, p, stream);
         default: return hipErrorInvalidValue;
         }
     }
     switch (p.tile.variant) {
     case 0: return launch_one<DT_BF16, 256, 256, 2, 2, 4, 32>(g, p, stream);
-    case 1: return launch_one<DT_BF16, 128, 128, 2, 2, 4, 32>(g, p, stream);
+    case 1: return launch_any_layout<DT_BF16, 128, 128, 2, 2, 4, 32>(g, p, stream);
     case 2: return launch_one<DT_BF16, 256, 128, 2, 2, 4, 32>(g, p, stream);
     case 3: return launch_one<DT_BF16, 256, 128, 2, 2, 3, 32>(g, p, stream);
     case 4: return launch_one<DT_BF16, 128, 256, 2, 2, 3, 32>(g, p, stream);
-    case 5: return launch_one<DT_BF16, 256, 256, 2, 2, 2, 64>(g, p, stream);
+    case 5: return launch_any_layout<DT_BF16, 256, 256, 2, 2, 2, 64>(g, p, stream);
     case 6: return launch_one<DT_BF16, 128, 128, 2, 2, 3, 64>(g, p, stream);
     case 7: return launch_one<DT_BF16, 256, 128, 2, 2, 3, 64>(g, p, stream);
     case 8: return launch_one<DT_BF16, 128, 256, 2, 2, 2, 32>(g, p, stream);

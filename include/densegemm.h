@@ -83,8 +83,9 @@ typedef enum { DG_ACT_NONE = 0, DG_ACT_GELU_ERF = 1, DG_ACT_GELU_TANH = 2 } dg_a
  * leading dimensions and batch strides multiple of 4; VALU_F32 (the
  * register-tiled vector-FMA kernel) takes the same operands and is used
  * only when asked for.  bf16 and fp16 inputs go to their matrix-core kernel
- * (MFMA_BF16, MFMA_F16) when A is row-major and B column-major, both
- * 16-byte aligned with leading dimensions and batch strides multiple of 8.
+ * (MFMA_BF16, MFMA_F16) in any order of A and B, both 16-byte aligned with
+ * leading dimensions and batch strides multiple of 8 (a column-major A or
+ * row-major B is transposed on its way from LDS to the matrix cores).
  * Forcing a family whose requirements the operands do not meet returns
  * DG_ERROR_NOT_SUPPORTED. */
 typedef enum {

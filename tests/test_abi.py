@@ -247,8 +247,10 @@ def test_f16_plans():
         with pytest.raises(dg.DgError) as e:
             dg.dg_gemm_describe(_desc(a_type=a, b_type=a, b_order="col", algo=algo))
         assert e.value.status == dg.DG_ERROR_NOT_SUPPORTED
-    # fp16 outside the matrix-core layout goes to the generic kernel
-    assert "kernel=generic" in dg.dg_gemm_describe(_desc(a_type="f16", b_type="f16"))
+    # fp16 in any order of A and B goes to its matrix-core kernel; with a
+    # leading dimension off the 16-byte grid, to the generic kernel
+    assert "kernel=mfma_f16" in dg.dg_gemm_describe(_desc(a_type="f16", b_type="f16"))
+    assert "kernel=generic" in dg.dg_gemm_describe(_desc(a_type="f16", b_type="f16", lda=36))
     # fp16 pointers need 2-byte alignment
     assert _gemm_status(_desc(a_type="f16", b_type="f16", c_type="f16"), C=PC + 1) == \
         dg.DG_ERROR_INVALID_VALUE
@@ -261,17 +263,38 @@ def test_f16_plans():
 
 def test_layouts_outside_the_fast_paths_use_the_generic_kernel():
     assert "kernel=generic" in dg.dg_gemm_describe(_desc(lda=33))     # ld not a multiple of 4
-    assert "kernel=generic" in dg.dg_gemm_describe(
-        _desc(a_type="bf16", a_order="col"))                          # bf16 A not K-contiguous
     d = _desc(a_type="bf16", b_order="col", lda=36)                    # lda not a multiple of 8
     assert "kernel=generic" in dg.dg_gemm_describe(d)
-    for bad in [_desc(a_type="bf16", algo=dg.DG_ALGO_MFMA_BF16),      # B not column-major
+    for bad in [_desc(a_type="bf16", lda=36, algo=dg.DG_ALGO_MFMA_BF16),  # lda % 8 != 0
                 _desc(lda=33, algo=dg.DG_ALGO_MFMA_F32),                  # ld not a multiple of 4
                 _desc(lda=33, algo=dg.DG_ALGO_VALU_F32),
                 _desc(a_type="bf16", b_order="col", algo=dg.DG_ALGO_VALU_F32)]:
         with pytest.raises(dg.DgError) as e:
             dg.dg_gemm_describe(bad)
         assert e.value.status == dg.DG_ERROR_NOT_SUPPORTED
+
+
+@pytest.mark.parametrize("a_order,b_order", [("row", "row"), ("col", "col"), ("col", "row"),
+                                             ("row", "col")])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_every_16bit_layout_runs_on_the_matrix_cores(a_order, b_order, dt, monkeypatch):
+    """Any order of A and B takes the 16-bit matrix-core kernel; an M- or
+    N-contiguous operand only on the two tiles of the automatic choice,
+    whatever the tuned table or a forced tile say."""
+    fam = "mfma_bf16" if dt == "bf16" else "mfma_f16"
+    for M, N, K, tile in [(4096, 4096, 4096, "256x256"), (300, 260, 200, "128x128")]:
+        up8 = lambda v: -(-v // 8) * 8     # noqa: E731
+        d = dg.make_desc(M, N, K, a_type=dt, a_order=a_order, b_order=b_order, c_type=dt,
+                         lda=up8(K if a_order == "row" else M),
+                         ldb=up8(N if b_order == "row" else K))
+        text = dg.dg_gemm_describe(d, 1 << 34)
+        assert f"kernel={fam}" in text and f"tile={fam}_{tile}" in text, text
+    if (a_order, b_order) != ("row", "col"):
+        monkeypatch.setenv("DG_FORCE_TILE", f"{fam}_256x128x32_w2x2_s4")
+        d = dg.make_desc(4096, 4096, 4096, a_type=dt, a_order=a_order, b_order=b_order)
+        text = dg.dg_gemm_describe(d, 1 << 34)
+        assert "tile=" + fam + "_256x256" in text or "tile=" + fam + "_128x128" in text, text
+        assert "tuned=0" in text
 
 
 def test_batch_strides_ignored_for_a_single_matrix():
