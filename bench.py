@@ -614,6 +614,153 @@ def _summary(workload, r, knobs=()):
     return rec
 
 
+# ---- tile-order ablation ------------------------------------------------------
+# Group height G of the grouped tile order x XCD remap on / off, on the two
+# headline problems and one whose operands exceed the Infinity Cache
+# ("GEMM Kernel Optimization", L2 Cache Grouping and Common Pitfalls on
+# GROUP_SIZE_M = 1).
+ABLATION_WORKLOADS = ("c2", "c3", "big8192")
+ABLATION_GROUPS = (1, 4, 8, 16)
+ABLATION_REMAP = (1, -1)          # descriptor xcd_remap: 1 on, -1 off
+ABLATION_CHILD_CALLS = 4          # per combination in the counter passes (first one dropped)
+
+
+def _ablation_problems():
+    import workloads as W
+    from workloads.device import DeviceProblem
+    for w in ABLATION_WORKLOADS:
+        p = W.WORKLOADS[w]
+        log(f"[ablation] {w}: generating {p.name}")
+        x = W.make_inputs(p)
+        dp = DeviceProblem(p, x)
+        del x
+        yield w, dp
+        del dp
+
+
+def _set_order(dp, g, r):
+    dp.desc.group_m = g
+    dp.desc.xcd_remap = r
+
+
+def ablation_timing(steps, settle):
+    """Sustained kernel time of every combination, timed in two passes
+    (combinations in order, then reversed) whose means are averaged, so a
+    slow drift of the clock does not favour the first or last."""
+    import torch
+    stream = torch.cuda.current_stream()
+    res = {}
+    for w, dp in _ablation_problems():
+        combos = [(g, r) for g in ABLATION_GROUPS for r in ABLATION_REMAP]
+        for order in (combos, combos[::-1]):
+            for g, r in order:
+                _set_order(dp, g, r)
+                for _ in range(settle):
+                    dp.run(stream.cuda_stream)
+                _, per = run_window(dp, stream, steps)
+                res.setdefault((w, g, r), []).append(sum(per) / len(per))
+        log(f"[ablation] {w}: {dp.describe()}")
+    return {k: sum(v) / len(v) for k, v in res.items()}
+
+
+def ablation_child():
+    """Every combination in a fixed order, ABLATION_CHILD_CALLS calls each,
+    nothing else on the GPU between them: the dispatch order of the GEMM
+    kernels identifies the combination in a counter pass."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for w, dp in _ablation_problems():
+        for g in ABLATION_GROUPS:
+            for r in ABLATION_REMAP:
+                _set_order(dp, g, r)
+                for _ in range(ABLATION_CHILD_CALLS):
+                    dp.run(stream.cuda_stream)
+                torch.cuda.synchronize()
+
+
+def run_ablation(steps, settle, tmp, out_dir=PROFILES):
+    import subprocess
+    import workloads as W
+    from dense_gemm_10_amd import accounting as acc
+    times = ablation_timing(steps, settle)
+    combos = [(w, g, r) for w in ABLATION_WORKLOADS for g in ABLATION_GROUPS
+              for r in ABLATION_REMAP]
+    counters = {}
+    cmds = {}
+    scale = {}
+    for name, pmc in (("tcc", ["TCC_HIT_sum", "TCC_MISS_sum"]), ("FETCH_SIZE", ["FETCH_SIZE"]),
+                      ("WRITE_SIZE", ["WRITE_SIZE"])):
+        out = os.path.join(tmp, name)
+        cmd = _rocprof(["--pmc"] + pmc, out, timeout_s=300) + ["--ablation-child"]
+        log(f"[ablation] {' '.join(cmd)}")
+        subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL)
+        cmds[name] = _shown(cmd, tmp)
+        rows = [r for r in _csv_rows(out, "counter_collection.csv") if "gemm_" in r["Kernel_Name"]]
+        for cn in pmc:
+            per = {}
+            for r in rows:
+                if r["Counter_Name"] == cn:
+                    per[int(r["Dispatch_Id"])] = per.get(int(r["Dispatch_Id"]), 0.0) + \
+                        float(r["Counter_Value"])
+            seq = [per[k] for k in sorted(per)]
+            if len(seq) != len(combos) * ABLATION_CHILD_CALLS:
+                raise RuntimeError(f"{cn}: {len(seq)} GEMM dispatches, expected "
+                                   f"{len(combos) * ABLATION_CHILD_CALLS}")
+            for i, c in enumerate(combos):
+                chunk = seq[i * ABLATION_CHILD_CALLS + 1:(i + 1) * ABLATION_CHILD_CALLS]
+                counters.setdefault(c, {})[cn] = sum(chunk) / len(chunk)
+        if name in ("FETCH_SIZE", "WRITE_SIZE"):
+            out_c = os.path.join(tmp, name + "_copy")
+            cmd_c = _rocprof(["--pmc", name], out_c) + ["--workload", "copy", "--steps", "3",
+                                                         "--warmup", "1"]
+            subprocess.run(cmd_c, check=True, stdout=subprocess.DEVNULL)
+            copy_kib, _ = _per_dispatch(_csv_rows(out_c, "counter_collection.csv"), "copy")
+            scale[name] = (512 << 20) / (copy_kib * 1024.0)
+            cmds[name + "_copy"] = _shown(cmd_c, tmp)
+    table = []
+    for c in combos:
+        w, g, r = c
+        p = W.WORKLOADS[w]
+        k = counters[c]
+        hit, miss = k["TCC_HIT_sum"], k["TCC_MISS_sum"]
+        ms = times[c]
+        table.append({"workload": w, "name": p.name, "group_m": g, "xcd_remap": r == 1,
+                      "kernel_us": ms * 1e3, "tflops": p.flops() / (ms * 1e-3) / 1e12,
+                      "frac_of_peak": p.flops() / (ms * 1e-3) / acc.compute_peak_for(p),
+                      "l2_hit_rate": hit / (hit + miss) if hit + miss else None,
+                      "l2_misses": miss,
+                      "fetch_bytes": k["FETCH_SIZE"] * 1024 * scale["FETCH_SIZE"],
+                      "write_bytes": k["WRITE_SIZE"] * 1024 * scale["WRITE_SIZE"],
+                      "algorithmic_bytes": acc.problem_bytes(p)})
+    result = {"table": table, "commands": cmds, "scale": scale, "steps": steps, "settle": settle,
+              "kernel_source_hash": kernel_source_hash()}
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "tile_order_ablation.json"), "w") as f:
+        json.dump(result, f, indent=1)
+    lines = ["# Tile-order ablation: group height x XCD remap", "",
+             "Made by `python3 bench.py --ablation` from the repository root. Kernel time: mean "
+             f"of per-call HIP event pairs over {steps} calls after {settle} untimed ones, per "
+             "combination, averaged over two passes (combinations in order, then reversed). "
+             "Counters: the commands below ($OUT is a temporary folder), over "
+             f"{ABLATION_CHILD_CALLS - 1} calls per combination after one untimed; FETCH_SIZE "
+             f"x {scale['FETCH_SIZE']:.3f} and WRITE_SIZE x {scale['WRITE_SIZE']:.3f} "
+             "(a 512 MiB device copy's reading).", "",
+             f"Kernel sources hash: `{result['kernel_source_hash']}`", "",
+             "| problem | G | XCD remap | kernel us | TFLOP/s | of peak | L2 hit | L2 misses "
+             "| HBM fetch MB | HBM write MB | algorithmic MB |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for t in table:
+        lines.append(f"| {t['name']} | {t['group_m']} | {'on' if t['xcd_remap'] else 'off'} | "
+                     f"{t['kernel_us']:.1f} | {t['tflops']:.1f} | {t['frac_of_peak']:.3f} | "
+                     f"{t['l2_hit_rate']:.3f} | {t['l2_misses']:.3g} | "
+                     f"{t['fetch_bytes'] / 1e6:.1f} | {t['write_bytes'] / 1e6:.1f} | "
+                     f"{t['algorithmic_bytes'] / 1e6:.1f} |")
+    lines += ["", "Commands:", ""] + [f"- {k}: `{v}`" for k, v in cmds.items()] + [""]
+    with open(os.path.join(out_dir, "tile_order_ablation.md"), "w") as f:
+        f.write("\n".join(lines))
+    return result
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -639,8 +786,23 @@ def main():
                     help="run rocprofv3 (kernel trace, FETCH_SIZE, WRITE_SIZE, L2, utilisation) "
                          "on this workload and write profiles/traffic_<tag>.json and a summary")
     ap.add_argument("--profile-dir", default=PROFILES,
-                    help="where --collect-profile writes (default: profiles/)")
+                    help="where --collect-profile and --ablation write (default: profiles/)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="tile-order ablation (group height x XCD remap) with kernel times and "
+                         "L2 / HBM counters; writes profiles/tile_order_ablation.md")
+    ap.add_argument("--ablation-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+
+    if args.ablation_child:
+        ablation_child()
+        return
+    if args.ablation:
+        import tempfile
+        with tempfile.TemporaryDirectory(dir=os.environ.get("TMPDIR", "/tmp")) as tmp:
+            r = run_ablation(50, 100, tmp, args.profile_dir)
+        print(json.dumps({"ablation": [{k: v for k, v in t.items() if k != "name"}
+                                       for t in r["table"]]}), flush=True)
+        return
 
     knobs = []
     for flag, v in (("--algo", args.algo), ("--group-m", args.group_m),
@@ -708,7 +870,7 @@ def main():
             v = time_workload("c2", K, Wm, ST, Ks, clock_s=CS, algo=dg.DG_ALGO_VALU_F32)
             extras["c2_valu"] = _summary("c2", v, ["--algo", str(dg.DG_ALGO_VALU_F32)])
             del v
-        for key in ("c1", "c4", "c5", "flat16"):
+        for key in ("c1", "c3_brow", "c4", "c5", "flat16"):
             if key in (args.workload, args.secondary):
                 continue
             r = time_workload(key, K, Wm, ST, Ks)

@@ -38,6 +38,11 @@ SOURCES = [
     "kernel_generic.hip",
     "kernel_valu_f32.hip",
     "kernel_mfma16.hip",
+    "kernel_mfma16_bf16a.hip",
+    "kernel_mfma16_bf16b.hip",
+    "kernel_mfma16_f16.hip",
+    "kernel_mfma16_mn256.hip",
+    "kernel_mfma16_mn128.hip",
     "kernel_mfma_f32.hip",
     "kernel_sliver.hip",
 ]
@@ -61,7 +66,7 @@ def build(verbose=False, defines=(), out=None):
     obj_dir = OUT_DIR if not defines else os.path.join(OUT_DIR, "opt_" + "_".join(
         d.replace("=", "-") for d in defines))
     os.makedirs(obj_dir, exist_ok=True)
-    workers = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    workers = min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(workers) as ex:
         objs = list(ex.map(lambda s: _compile(s, defines, obj_dir), SOURCES))
     tmp = lib + f".tmp{os.getpid()}"

@@ -237,16 +237,23 @@ __device__ __forceinline__ void tile_epilogue_whole(const GemmArgs &g, char *out
     auto shift = [&](int r) { return SHIFTED ? (d0 + r * dl) & (VEC - 1) : 0; };
     // chunk row cr of chunk c is tile row (cr / 32) * TM + c * 32 + cr % 32
     auto tile_row = [&](int c, int cr) { return (cr / 32) * TM + c * 32 + cr % 32; };
+    // Every run of a thread is at tile row rt plus a multiple of 8 (32-row
+    // blocks, TM-row wave blocks and RSTEP-row steps are all multiples of
+    // VEC), so with the row misalignment stepping by dl per row, all of them
+    // share one shift, one block slot and so one set of VEC columns: the
+    // thread's bias values are read once, into registers.
+    const int sh_t = shift(rt);
+    const int col_t = (js + (sh_t != 0 ? 1 : 0)) * VEC - sh_t;   // first column of the runs
     float bias[VEC];
     const bool has_bias = !PARTIAL && g.bias;
     if (has_bias) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            bias[e] = col_t + e < BN ? load_as_f32(g.bias, g.bias_type, n0 + col_t + e) : 0.0f;
         if (SHIFTED) {
+            // the head and tail elements, one by one
             for (int t = tid; t < BN; t += NT)
                 bias_s[t] = load_as_f32(g.bias, g.bias_type, n0 + t);
-        } else {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                bias[e] = load_as_f32(g.bias, g.bias_type, n0 + js * VEC + e);
         }
     }
     const bool read_c = !PARTIAL && g.beta != 0.0f;
@@ -306,14 +313,27 @@ __device__ __forceinline__ void tile_epilogue_whole(const GemmArgs &g, char *out
                     if (full[u])
                         cin[u] = *(const uint4 *)(rowbase + (int64_t)trow[u] * ld_bytes + (int64_t)col[u] * ES);
             }
+            // A 16-bit output's run is 8 staged floats, two 16-byte halves
+            // 32 bytes apart from the next slot's: slots j and j + 8 would
+            // share bank groups.  Slots with bit 3 set read their halves in
+            // the other order, so the 16 lanes of one read cover all 16
+            // groups.
             float v[GROUP][VEC];
+            const bool swap_halves = VEC == 8 && ((js >> 3) & 1);
 #pragma unroll
-            for (int u = 0; u < GROUP; ++u)
-#pragma unroll
-                for (int e = 0; e < VEC; e += 4) {
-                    const float4 x = *(const float4 *)&rdrow[(q0 + u) * RSTEP * EP_LD + blk[u] * VEC + e];
-                    v[u][e] = x.x; v[u][e + 1] = x.y; v[u][e + 2] = x.z; v[u][e + 3] = x.w;
+            for (int u = 0; u < GROUP; ++u) {
+                const float *rp = &rdrow[(q0 + u) * RSTEP * EP_LD + blk[u] * VEC];
+                if constexpr (VEC == 8) {
+                    const float4 x0 = *(const float4 *)(rp + (swap_halves ? 4 : 0));
+                    const float4 x1 = *(const float4 *)(rp + (swap_halves ? 0 : 4));
+                    const float4 lo = swap_halves ? x1 : x0, hi = swap_halves ? x0 : x1;
+                    v[u][0] = lo.x; v[u][1] = lo.y; v[u][2] = lo.z; v[u][3] = lo.w;
+                    v[u][4] = hi.x; v[u][5] = hi.y; v[u][6] = hi.z; v[u][7] = hi.w;
+                } else {
+                    const float4 x = *(const float4 *)rp;
+                    v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
                 }
+            }
             // Each step covers the whole group, so every uniform branch
             // (beta, bias, activation) is taken once per group, not per run.
             if (!PARTIAL) {
@@ -338,14 +358,8 @@ __device__ __forceinline__ void tile_epilogue_whole(const GemmArgs &g, char *out
 #pragma unroll
                     for (int u = 0; u < GROUP; ++u)
 #pragma unroll
-                        for (int e = 0; e < VEC; ++e) {
-                            if (SHIFTED) {
-                                const int bc = col[u] + e;   // past BN only in a slot without a block
-                                v[u][e] += bias_s[bc < BN ? bc : BN - 1];
-                            } else {
-                                v[u][e] += bias[e];
-                            }
-                        }
+                        for (int e = 0; e < VEC; ++e)
+                            v[u][e] += bias[e];
                 }
                 auto act_all = [&](auto A) {
 #pragma unroll

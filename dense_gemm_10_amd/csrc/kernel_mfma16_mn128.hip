@@ -1,0 +1,23 @@
+// Instantiations of the 16-bit matrix-core GEMM (mfma16.hpp): an M- or N-contiguous operand, 128 x 128 tile, bf16 and fp16.
+#include "mfma16.hpp"
+
+namespace dg {
+
+template <int T>
+hipError_t launch_mn128(const GemmArgs &g, const Plan &p, hipStream_t stream)
+{
+    const bool at = g.a_col != 0, bt = g.b_col == 0;
+    if (at && bt)
+        return launch_layout<T, 128, 128, 2, 2, 4, 32, true, true>(g, p, stream);
+    if (at)
+        return launch_layout<T, 128, 128, 2, 2, 4, 32, true, false>(g, p, stream);
+    return launch_layout<T, 128, 128, 2, 2, 4, 32, false, true>(g, p, stream);
+}
+
+hipError_t launch_mfma16_mn128(const GemmArgs &g, const Plan &p, hipStream_t stream)
+{
+    return g.ab_type == DT_F16 ? launch_mn128<DT_F16>(g, p, stream)
+                               : launch_mn128<DT_BF16>(g, p, stream);
+}
+
+} // namespace dg

@@ -161,7 +161,8 @@ typedef enum {
  *                   S > 1: split K into S slices (needs workspace); with
  *                   schedule STREAM_K, the K slices of each tail tile.
  *   group_m         output-tile group height of the swizzled tile order; 0
- *                   picks the default (8).  1 gives plain row-major order.
+ *                   picks the default (4, measured best with the XCD
+ *                   remap).  1 gives plain row-major order.
  *   algo            dg_algo; 0 = automatic choice.
  *   xcd_remap       1 (default when 0) spreads consecutive tile groups over
  *                   the chip's 8 XCDs so each XCD's L2 sees a contiguous

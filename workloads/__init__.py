@@ -217,6 +217,34 @@ WORKLOADS = {
         alpha=1.0, beta=0.0, has_bias=True, bias_type=F16, act=ACT_GELU_ERF,
         dist_a=("normal", 0.5), dist_b=("normal", 0.5),
         dist_bias=("uniform", -0.5, 0.5), seed=10),
+    # The bf16 4096^3 problem in the other three operand orders (PyTorch's
+    # default, both row-major, first): same sizes, values and output.
+    "c3_brow": Problem(
+        name="gemm_bf16_4096_arow_brow", M=4096, N=4096, K=4096,
+        a_type=BF16, b_type=BF16, c_type=BF16,
+        a_order=ROW, b_order=ROW, c_order=ROW,
+        alpha=1.0, beta=0.0,
+        dist_a=("normal", 1.0), dist_b=("normal", 1.0), seed=3),
+    "c3_acol": Problem(
+        name="gemm_bf16_4096_acol_bcol", M=4096, N=4096, K=4096,
+        a_type=BF16, b_type=BF16, c_type=BF16,
+        a_order=COL, b_order=COL, c_order=ROW,
+        alpha=1.0, beta=0.0,
+        dist_a=("normal", 1.0), dist_b=("normal", 1.0), seed=3),
+    "c3_acol_brow": Problem(
+        name="gemm_bf16_4096_acol_brow", M=4096, N=4096, K=4096,
+        a_type=BF16, b_type=BF16, c_type=BF16,
+        a_order=COL, b_order=ROW, c_order=ROW,
+        alpha=1.0, beta=0.0,
+        dist_a=("normal", 1.0), dist_b=("normal", 1.0), seed=3),
+    # A problem whose operands (128 MiB each) and output exceed the 256 MB
+    # Infinity Cache: where the grouped tile order should show in time.
+    "big8192": Problem(
+        name="gemm_bf16_8192", M=8192, N=8192, K=8192,
+        a_type=BF16, b_type=BF16, c_type=BF16,
+        a_order=ROW, b_order=COL, c_order=ROW,
+        alpha=1.0, beta=0.0,
+        dist_a=("normal", 1.0), dist_b=("normal", 1.0), seed=11),
     "tail4352": Problem(
         name="gemm_bf16_4352x4352x8192", M=4352, N=4352, K=8192,
         a_type=BF16, b_type=BF16, c_type=BF16,
