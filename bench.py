@@ -82,28 +82,32 @@ class Flusher:
 
 
 def run_window(dp, stream, steps, flush=None):
-    """`steps` timed calls.  Returns (window ms per call, per-call ms list):
-    the window time runs from the first call's start event to the last
-    call's end event (launch gaps included), divided by `steps`; each call
-    also has its own event pair.  With `flush`, the flush runs before each
-    call, outside its event pair, and the window time is the sum of the
-    pairs."""
+    """`steps` timed calls.  Returns (ms per call, per-call ms list).
+    Without `flush` the calls run back to back between one pair of events
+    on the launch stream (an event recorded between calls would add its
+    own gap to every call), and the list holds that mean once per call.
+    With `flush`, the flush runs before each call, outside the call's own
+    event pair, and the mean is over those pairs."""
     import torch
-    pairs = [_event_pair() for _ in range(steps)]
     torch.cuda.synchronize()
+    if flush is None:
+        s, e = _event_pair()
+        s.record(stream)
+        for _ in range(steps):
+            dp.run(stream.cuda_stream)
+        e.record(stream)
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / steps
+        return ms, [ms] * steps
+    pairs = [_event_pair() for _ in range(steps)]
     for s, e in pairs:
-        if flush is not None:
-            flush()
+        flush()
         s.record(stream)
         dp.run(stream.cuda_stream)
         e.record(stream)
     torch.cuda.synchronize()
     per_call = [s.elapsed_time(e) for s, e in pairs]
-    if flush is not None:
-        window = sum(per_call) / steps
-    else:
-        window = pairs[0][0].elapsed_time(pairs[-1][1]) / steps
-    return window, per_call
+    return sum(per_call) / steps, per_call
 
 
 def _smi_gfx_clocks():
@@ -155,10 +159,11 @@ def clock_window(dp, stream, seconds=2.5):
 
 
 def _window_stats(window_ms, per_call):
+    """kernel_ms_mean: the time per call the roofline uses (the window mean
+    for back-to-back calls; the mean of per-call event pairs with a flush)."""
     srt = sorted(per_call)
     return {"ms_per_step": window_ms, "kernel_ms_mean": sum(per_call) / len(per_call),
-            "kernel_ms_min": srt[0], "kernel_ms_median": srt[len(srt) // 2],
-            "kernel_ms_max": srt[-1], "calls": len(per_call)}
+            "kernel_ms_min": srt[0], "kernel_ms_max": srt[-1], "calls": len(per_call)}
 
 
 def time_workload(name, steps, warmup, settle=0, steps_sustained=0, flush=None, clock_s=0.0,

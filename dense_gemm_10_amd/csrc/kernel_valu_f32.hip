@@ -17,8 +17,10 @@
 //   - loads are masked on the row/column bound and on the split's K range
 //     with zero fill; stores are masked on M and N ("Skill: Write a Triton
 //     GEMM Kernel", Required reasoning process step 5).
-// The library is built without packed-fp32 instructions, so every FMA is
-// a v_fma_f32: the ceiling is 64 FMA per clock per CU.
+// The library is built without packed-fp32 instructions; the inner loop's
+// FMAs are the two-operand accumulate form v_fmac_f32, which gfx950 issues
+// at twice the rate of v_fma_f32: the ceiling is 128 FMA per clock per CU,
+// the chip's published fp32 vector rate.
 //
 // Requirements checked on the host: fp32 A and B, 16-byte aligned base
 // pointers, lda, ldb and batch strides multiples of 4 elements.
