@@ -44,6 +44,7 @@ SOURCES = [
     "kernel_mfma16_mn256.hip",
     "kernel_mfma16_mn128.hip",
     "kernel_mfma_f32.hip",
+    "tiles_f32.cpp",
     "kernel_sliver.hip",
 ]
 

@@ -321,14 +321,6 @@ hipError_t launch_f32(const GemmArgs &g, const Plan &p, hipStream_t stream)
 
 // Entries 0 and 1 are the large and small tiles of the automatic choice;
 // the 32-deep ones are selectable by name and by the tuned table.
-const TileConfig kMfmaF32Tiles[] = {
-    {256, 256, 16, 256, 0, "mfma_f32_256x256x16_w2x2"},
-    {128, 128, 16, 256, 1, "mfma_f32_128x128x16_w2x2"},
-    {256, 256, 32, 256, 2, "mfma_f32_256x256x32_w2x2"},
-    {128, 128, 32, 256, 3, "mfma_f32_128x128x32_w2x2"},
-};
-const int kNumMfmaF32Tiles = 4;
-
 hipError_t launch_mfma_f32(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
     switch (p.tile.variant) {
