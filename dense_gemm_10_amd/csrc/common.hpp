@@ -90,36 +90,108 @@ __device__ __forceinline__ float load_as_f32(const void *base, int32_t type, int
 }
 
 // ---- activation ------------------------------------------------------------
-// GELU with the exact normal CDF, x * Phi(x), Phi(x) = erfc(-x / sqrt 2) / 2.
-// erfc on z = |x| / sqrt 2 follows Abramowitz and Stegun, Handbook of
-// Mathematical Functions, formula 7.1.26: erfc(z) ~ t (a1 + t (a2 + t (a3 +
-// t (a4 + t a5)))) exp(-z^2) with t = 1 / (1 + p z), absolute error at most
-// 1.5e-7 for z >= 0.  Taking erfc directly (instead of 1 - erf) keeps the
-// negative side free of cancellation; one exp2, one reciprocal and no
-// branches, where the math library's erff is a long branchy sequence.
+// GELU with the exact normal CDF, x * Phi(x), where Phi(x) = 1 - h for
+// x >= 0 and h for x < 0, with h = Phi(-|x|) = erfc(z) / 2, z = |x| / sqrt 2:
+// both sides free of cancellation.  erfc follows Abramowitz and Stegun,
+// Handbook of Mathematical Functions, formula 7.1.26: erfc(z) ~ t (a1 + t
+// (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2) with t = 1 / (1 + p z), absolute
+// error at most 1.5e-7 for z >= 0; here p z = (p / sqrt 2) |x|, the a_i are
+// halved (exactly) to give h directly, and exp(-z^2) = 2^(-x^2 log2(e) / 2):
+// one reciprocal, one exp2 and no branches, where the math library's erff
+// is a long branchy sequence.  +inf gives +inf, -inf gives NaN (x * Phi(x)
+// in IEEE arithmetic) and NaN stays NaN.
+struct GeluErf {
+    static constexpr float kP = 0.3275911f * 0.70710678118654752f;
+    static constexpr float kE = -0.72134752044448170f;          // -log2(e) / 2
+    static constexpr float kA1 = 0.5f * 0.254829592f, kA2 = 0.5f * -0.284496736f,
+                           kA3 = 0.5f * 1.421413741f, kA4 = 0.5f * -1.453152027f,
+                           kA5 = 0.5f * 1.061405429f;
+};
+
+// Keeps the compiler's scheduler from moving instructions across this
+// point (no instruction is emitted).
+__device__ __forceinline__ void sched_fence()
+{
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// N values at once, each step over all of them before the next, so that
+// the reciprocal and exp2 latencies of one value overlap the others' work.
+template <int N>
+__device__ __forceinline__ void gelu_erf_n(float (&v)[N])
+{
+    float t[N], e[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        t[i] = __builtin_amdgcn_rcpf(fmaf(fabsf(v[i]), GeluErf::kP, 1.0f));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        e[i] = __builtin_amdgcn_exp2f(GeluErf::kE * v[i] * v[i]);
+    if (N > 1)
+        sched_fence();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        float q = fmaf(t[i], GeluErf::kA5, GeluErf::kA4);
+        q = fmaf(t[i], q, GeluErf::kA3);
+        q = fmaf(t[i], q, GeluErf::kA2);
+        q = fmaf(t[i], q, GeluErf::kA1);
+        q *= t[i];
+        const float h = q * e[i];                  // Phi(-|x|)
+        const float g = fmaf(-q, e[i], 1.0f);      // 1 - h
+        v[i] *= v[i] >= 0.0f ? g : h;
+    }
+}
+
 __device__ __forceinline__ float gelu_erf(float x)
 {
-    const float z = fabsf(x) * 0.70710678118654752f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-    float q = fmaf(t, 1.061405429f, -1.453152027f);
-    q = fmaf(t, q, 1.421413741f);
-    q = fmaf(t, q, -0.284496736f);
-    q = fmaf(t, q, 0.254829592f);
-    // exp(-z^2) = 2^(-x^2 log2(e) / 2)
-    const float e = __builtin_amdgcn_exp2f(-0.72134752044448170f * x * x);
-    const float h = 0.5f * t * q * e;          // erfc(z) / 2 = Phi(-|x|)
-    return x * (x >= 0.0f ? 1.0f - h : h);
+    float v[1] = {x};
+    gelu_erf_n<1>(v);
+    return v[0];
 }
 
 // GELU with the tanh approximation of the normal CDF:
 // (1 + tanh(y)) / 2 with y = sqrt(2/pi) (x + 0.044715 x^3).  Uses the exact
-// identity (1 + tanh(y)) / 2 = 1 / (1 + exp(-2y)), which has no cancellation.
+// identity (1 + tanh(y)) / 2 = 1 / (1 + exp(-2y)), which has no
+// cancellation; exp(-2y) = 2^(-2y log2(e)).
+template <int N>
+__device__ __forceinline__ void gelu_tanh_n(float (&v)[N])
+{
+    float e[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float y = 0.79788456080286536f * fmaf(0.044715f * v[i], v[i] * v[i], v[i]);
+        e[i] = __builtin_amdgcn_exp2f(-2.8853900817779268f * y);
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = v[i] * __builtin_amdgcn_rcpf(1.0f + e[i]);
+}
+
 __device__ __forceinline__ float gelu_tanh(float x)
 {
-    const float y = 0.79788456080286536f * fmaf(0.044715f * x, x * x, x);
-    // exp(-2y) = 2^(-2y log2(e))
-    const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * y);
-    return x * __builtin_amdgcn_rcpf(1.0f + e);
+    float v[1] = {x};
+    gelu_tanh_n<1>(v);
+    return v[0];
+}
+
+// The activation on N values; ACT is a compile-time dg_act.
+template <int32_t ACT, int N>
+__device__ __forceinline__ void activate_n(float (&v)[N])
+{
+    if constexpr (ACT == ACT_GELU_ERF)
+        gelu_erf_n<N>(v);
+    else if constexpr (ACT == ACT_GELU_TANH)
+        gelu_tanh_n<N>(v);
+}
+
+// The activation on N values, act a run-time (uniform) dg_act.
+template <int N>
+__device__ __forceinline__ void activate_n(float (&v)[N], int32_t act)
+{
+    if (act == ACT_GELU_ERF)
+        gelu_erf_n<N>(v);
+    else if (act == ACT_GELU_TANH)
+        gelu_tanh_n<N>(v);
 }
 
 __device__ __forceinline__ float activate(float x, int32_t act)

@@ -34,9 +34,11 @@ __device__ __forceinline__ void run_epilogue(const GemmArgs &g, int64_t b, int64
                                              int64_t lim, bool col_major, float (&v)[VEC],
                                              const float *bias_run)
 {
+    if (g.alpha != 1.0f) {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e)
-        v[e] *= g.alpha;
+        for (int e = 0; e < VEC; ++e)
+            v[e] *= g.alpha;
+    }
     if (g.beta != 0.0f) {
         const int64_t base = b * g.sc + go * g.ldc + gi;
 #pragma unroll
@@ -49,11 +51,8 @@ __device__ __forceinline__ void run_epilogue(const GemmArgs &g, int64_t b, int64
         for (int e = 0; e < VEC; ++e)
             v[e] += col_major ? bias_run[0] : bias_run[e];
     }
-    if (g.act != ACT_NONE) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            v[e] = activate(v[e], g.act);
-    }
+    if (g.act != ACT_NONE)
+        activate_n<VEC>(v, g.act);
 }
 
 // Store rows [r0, r0 + ROWS) of a BM x BN output tile from an LDS chunk
@@ -337,11 +336,13 @@ __device__ __forceinline__ void tile_epilogue_whole(const GemmArgs &g, char *out
             // Each step covers the whole group, so every uniform branch
             // (beta, bias, activation) is taken once per group, not per run.
             if (!PARTIAL) {
+                if (g.alpha != 1.0f) {
 #pragma unroll
-                for (int u = 0; u < GROUP; ++u)
+                    for (int u = 0; u < GROUP; ++u)
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        v[u][e] *= g.alpha;
+                        for (int e = 0; e < VEC; ++e)
+                            v[u][e] *= g.alpha;
+                }
                 if (read_c) {
 #pragma unroll
                     for (int u = 0; u < GROUP; ++u) {
@@ -364,9 +365,7 @@ __device__ __forceinline__ void tile_epilogue_whole(const GemmArgs &g, char *out
                 auto act_all = [&](auto A) {
 #pragma unroll
                     for (int u = 0; u < GROUP; ++u)
-#pragma unroll
-                        for (int e = 0; e < VEC; ++e)
-                            v[u][e] = activate(v[u][e], decltype(A)::value);
+                        activate_n<decltype(A)::value, VEC>(v[u]);
                 };
                 if (g.act == ACT_GELU_ERF)
                     act_all(std::integral_constant<int32_t, ACT_GELU_ERF>{});
@@ -515,11 +514,8 @@ __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out,
                         v[e] += bias_s[col < 0 ? 0 : (col < BN ? col : BN - 1)];
                     }
                 }
-                if (g.act != ACT_NONE) {
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        v[e] = activate(v[e], g.act);
-                }
+                if (g.act != ACT_NONE)
+                    activate_n<VEC>(v, g.act);
             }
             if (HALF_OUT) {
                 uint16_t h[VEC];
