@@ -11,6 +11,28 @@ namespace dg {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// 16-byte store of a final output: non-temporal, so that C streams out
+// towards memory instead of staying dirty in the L2s until the release at
+// the kernel's end writes it back (the output is written once and no
+// kernel of the call reads it).  Partials for a later reduction (PARTIAL
+// paths) keep the default policy: the next kernel reads them.
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+template <bool NT = true>
+__device__ __forceinline__ void store16(void *dst, uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3)
+{
+    if constexpr (NT)
+        __builtin_nontemporal_store((u32x4_nt){w0, w1, w2, w3}, (u32x4_nt *)dst);
+    else
+        *(uint4 *)dst = make_uint4(w0, w1, w2, w3);
+}
+
+template <bool NT = true>
+__device__ __forceinline__ void store16(void *dst, float v0, float v1, float v2, float v3)
+{
+    store16<NT>(dst, __float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2),
+                __float_as_uint(v3));
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
 // accesses, not for its global stores.  __syncthreads() also waits for every
 // outstanding global store (its release fence covers global memory), which
@@ -96,7 +118,7 @@ __device__ __forceinline__ void store_chunk(const GemmArgs &g, const TileCoord &
         if (OUT == DT_F32) {
             float *dst = (float *)g.C + off;
             if (full && ((uintptr_t)dst & 15) == 0) {
-                *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
+                store16(dst, v[0], v[1], v[2], v[3]);
             } else {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
@@ -114,7 +136,7 @@ __device__ __forceinline__ void store_chunk(const GemmArgs &g, const TileCoord &
 #pragma unroll
                 for (int e = 0; e < VEC / 2; ++e)
                     w[e] = (uint32_t)h[2 * e] | ((uint32_t)h[2 * e + 1] << 16);
-                *(uint4 *)dst = make_uint4(w[0], w[1], w[2], w[3]);
+                store16(dst, w[0], w[1], w[2], w[3]);
             } else {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
@@ -383,9 +405,9 @@ __device__ __forceinline__ void tile_epilogue_whole(const GemmArgs &g, char *out
                     for (int e = 0; e < 4; ++e)
                         w[e] = (uint32_t)f32_to_half<OUT>(v[u][2 * e]) |
                                ((uint32_t)f32_to_half<OUT>(v[u][2 * e + 1]) << 16);
-                    *(uint4 *)dst = make_uint4(w[0], w[1], w[2], w[3]);
+                    store16<!PARTIAL>(dst, w[0], w[1], w[2], w[3]);
                 } else {
-                    *(float4 *)dst = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
+                    store16<!PARTIAL>(dst, v[u][0], v[u][1], v[u][2], v[u][3]);
                 }
             }
         });
@@ -527,7 +549,7 @@ __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out,
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         w[e] = (uint32_t)h[2 * e] | ((uint32_t)h[2 * e + 1] << 16);
-                    *(uint4 *)dst = make_uint4(w[0], w[1], w[2], w[3]);
+                    store16<!PARTIAL>(dst, w[0], w[1], w[2], w[3]);
                 } else {
 #pragma unroll
                     for (int e = 0; e < VEC; ++e)
@@ -536,7 +558,7 @@ __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out,
                 }
             } else {
                 if (full) {
-                    *(float4 *)dst = make_float4(v[0], v[1], v[2], v[3]);
+                    store16<!PARTIAL>(dst, v[0], v[1], v[2], v[3]);
                 } else {
 #pragma unroll
                     for (int e = 0; e < VEC; ++e)

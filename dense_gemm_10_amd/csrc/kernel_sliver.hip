@@ -6,11 +6,14 @@
 // tiled kernel on the full tile columns and this kernel on the remaining
 // nrem <= kMaxSliver columns.  Each output is a dot product of a row of A
 // with a column of B ("La GEMM, de zero a cuBLAS", section 2.1: one output
-// element per K-length product), so one wavefront takes one row m: its 64
-// lanes stride along K with 16-byte loads of the K-contiguous A row, every
-// lane keeps nrem fp32 partial sums, the wavefront adds them up across
-// lanes, and the epilogue (alpha, beta * C, bias, activation, output
-// dtype) is applied once per output.
+// element per K-length product).  A wavefront takes kSliverRows rows of A:
+// its 64 lanes stride along K in 16-byte pieces, each K step loads the
+// sliver columns' B values once (one 16-byte load per column when B's
+// columns are K-contiguous and aligned) and every row's A piece, so all of
+// a step's loads are in flight together; every lane keeps rows x columns
+// fp32 partial sums, the wavefront adds them up across lanes, and one lane
+// per output applies the epilogue (alpha, beta * C, bias, activation,
+// output dtype).  Few, fuller workgroups: 4095 rows take 256.
 //
 // Requirements checked on the host: row-major A with 16-byte aligned rows
 // (lda a multiple of 16 bytes, aligned base).
@@ -20,97 +23,147 @@ namespace dg {
 
 namespace {
 
-constexpr int kSliverThreads = 256;        // 4 rows per workgroup
+constexpr int kSliverThreads = 256;        // 4 wavefronts
+constexpr int kSliverRows = 4;             // rows of A per wavefront
 
 template <int AB_TYPE>
-__device__ __forceinline__ float elem_f32(const void *p, int64_t i)
+__device__ __forceinline__ float elem_f32(const char *p, int64_t i)
 {
     if (AB_TYPE == DT_F32)
         return ((const float *)p)[i];
     return half_to_f32<AB_TYPE>(((const uint16_t *)p)[i]);
 }
 
-template <int AB_TYPE>
+// The VK values of a 16-byte piece as fp32.
+template <int AB_TYPE, int VK>
+__device__ __forceinline__ void unpack16(const uint4 q, float (&x)[VK])
+{
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < VK; ++e)
+        x[e] = AB_TYPE == DT_F32 ? __uint_as_float(w[e])
+                                 : half_to_f32<AB_TYPE>((uint16_t)(w[e / 2] >> (16 * (e % 2))));
+}
+
+// NR: columns the kernel is built for (nrem <= NR).
+template <int AB_TYPE, int NR>
 __global__ __launch_bounds__(kSliverThreads) void gemm_sliver_kernel(GemmArgs g, int64_t n0,
                                                                      int32_t nrem)
 {
-    constexpr int VK = AB_TYPE == DT_F32 ? 4 : 8;   // K elements per 16-byte load
+    constexpr int ES = AB_TYPE == DT_F32 ? 4 : 2;   // element size
+    constexpr int VK = 16 / ES;                     // K elements per 16-byte piece
+    constexpr int R = kSliverRows;
+    static_assert(R * NR <= 64, "one lane per output");
     const int lane = threadIdx.x & 63;
-    const int64_t m = (int64_t)blockIdx.x * (kSliverThreads / 64) + (threadIdx.x >> 6);
+    const int64_t m0 = ((int64_t)blockIdx.x * (kSliverThreads / 64) + (threadIdx.x >> 6)) * R;
     const int64_t b = blockIdx.y;
-    if (m >= g.M)
+    if (m0 >= g.M)
         return;                                     // whole wavefronts leave together
-    const char *arow = (const char *)g.A +
-                       (b * g.sa + m * g.lda) * (AB_TYPE == DT_F32 ? 4 : 2);
-    const void *B = (const char *)g.B + b * g.sb * (AB_TYPE == DT_F32 ? 4 : 2);
-    float acc[kMaxSliver];
+    const char *A = (const char *)g.A + b * g.sa * ES;
+    const char *B = (const char *)g.B + b * g.sb * ES;
+    // B's sliver columns K-contiguous with 16-byte aligned starts
+    const bool b_vec = g.b_col && ((((uintptr_t)B + (uintptr_t)(n0 * g.ldb * ES)) |
+                                    (uintptr_t)(g.ldb * ES)) & 15) == 0;
+    float acc[R][NR];
 #pragma unroll
-    for (int j = 0; j < kMaxSliver; ++j)
-        acc[j] = 0.0f;
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+            acc[r][j] = 0.0f;
     for (int64_t k = (int64_t)lane * VK; k < g.K; k += 64 * VK) {
-        float a[VK];
-        if (k + VK <= g.K) {
-            const uint4 q = *(const uint4 *)(arow + k * (AB_TYPE == DT_F32 ? 4 : 2));
-            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        const bool whole = k + VK <= g.K;
+        float bv[NR][VK];
 #pragma unroll
-            for (int e = 0; e < VK; ++e)
-                a[e] = AB_TYPE == DT_F32 ? __uint_as_float(w[e])
-                                         : half_to_f32<AB_TYPE>((uint16_t)(w[e / 2] >> (16 * (e % 2))));
-        } else {
-#pragma unroll
-            for (int e = 0; e < VK; ++e)
-                a[e] = k + e < g.K ? elem_f32<AB_TYPE>(arow, k + e) : 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < kMaxSliver; ++j) {
-            if (j >= nrem)
-                break;
+        for (int j = 0; j < NR; ++j) {
             const int64_t n = n0 + j;
+            if (j < nrem && b_vec && whole) {
+                unpack16<AB_TYPE, VK>(*(const uint4 *)(B + (n * g.ldb + k) * ES), bv[j]);
+            } else {
 #pragma unroll
-            for (int e = 0; e < VK; ++e) {
-                if (k + e < g.K) {
+                for (int e = 0; e < VK; ++e) {
                     const int64_t bi = g.b_col ? n * g.ldb + k + e : (k + e) * g.ldb + n;
-                    acc[j] = fmaf(a[e], elem_f32<AB_TYPE>(B, bi), acc[j]);
+                    bv[j][e] = j < nrem && k + e < g.K ? elem_f32<AB_TYPE>(B, bi) : 0.0f;
                 }
             }
         }
+        float av[R][VK];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t m = m0 + r < g.M ? m0 + r : g.M - 1;   // rows past M: any valid row, unused
+            const char *arow = A + m * g.lda * ES;
+            if (whole) {
+                unpack16<AB_TYPE, VK>(*(const uint4 *)(arow + k * ES), av[r]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < VK; ++e)
+                    av[r][e] = k + e < g.K ? elem_f32<AB_TYPE>(arow, k + e) : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int j = 0; j < NR; ++j)
+#pragma unroll
+                for (int e = 0; e < VK; ++e)
+                    acc[r][j] = fmaf(av[r][e], bv[j][e], acc[r][j]);
     }
     // sum over the wavefront's 64 lanes
 #pragma unroll
-    for (int j = 0; j < kMaxSliver; ++j) {
-        if (j >= nrem)
-            break;
-        float v = acc[j];
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1)
-            v += __shfl_xor(v, off, 64);
-        acc[j] = v;
-    }
-    if (lane < nrem) {
+        for (int j = 0; j < NR; ++j) {
+            if (j >= nrem)
+                break;
+            float v = acc[r][j];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1)
+                v += __shfl_xor(v, off, 64);
+            acc[r][j] = v;
+        }
+    // lane r * NR + j finishes output (m0 + r, n0 + j)
+    const int r = lane / NR, j = lane % NR;
+    if (lane < R * NR && j < nrem && m0 + r < g.M) {
         float v = 0.0f;
 #pragma unroll
-        for (int j = 0; j < kMaxSliver; ++j)
-            if (j == lane)
-                v = acc[j];
-        const int64_t n = n0 + lane;
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int jj = 0; jj < NR; ++jj)
+                if (rr == r && jj == j)
+                    v = acc[rr][jj];
+        const int64_t m = m0 + r, n = n0 + j;
         store_c(g, b, m, n, epilogue_value(g, b, m, n, v));
     }
+}
+
+template <int AB_TYPE>
+hipError_t launch_sliver_t(const GemmArgs &g, int64_t n0, int32_t nrem, hipStream_t stream)
+{
+    constexpr int rows_per_block = kSliverThreads / 64 * kSliverRows;
+    const dim3 grid((unsigned)((g.M + rows_per_block - 1) / rows_per_block),
+                    (unsigned)g.sched.batch),
+        block(kSliverThreads);
+    if (nrem <= 1)
+        hipLaunchKernelGGL((gemm_sliver_kernel<AB_TYPE, 1>), grid, block, 0, stream, g, n0, nrem);
+    else if (nrem <= 2)
+        hipLaunchKernelGGL((gemm_sliver_kernel<AB_TYPE, 2>), grid, block, 0, stream, g, n0, nrem);
+    else if (nrem <= 4)
+        hipLaunchKernelGGL((gemm_sliver_kernel<AB_TYPE, 4>), grid, block, 0, stream, g, n0, nrem);
+    else
+        hipLaunchKernelGGL((gemm_sliver_kernel<AB_TYPE, 8>), grid, block, 0, stream, g, n0, nrem);
+    return hipGetLastError();
 }
 
 } // namespace
 
 hipError_t launch_sliver(const GemmArgs &g, int64_t n0, int32_t nrem, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((g.M + kSliverThreads / 64 - 1) / (kSliverThreads / 64)),
-                    (unsigned)g.sched.batch),
-        block(kSliverThreads);
+    if (nrem < 1 || nrem > kMaxSliver)
+        return hipErrorInvalidValue;
     if (g.ab_type == DT_BF16)
-        hipLaunchKernelGGL((gemm_sliver_kernel<DT_BF16>), grid, block, 0, stream, g, n0, nrem);
-    else if (g.ab_type == DT_F16)
-        hipLaunchKernelGGL((gemm_sliver_kernel<DT_F16>), grid, block, 0, stream, g, n0, nrem);
-    else
-        hipLaunchKernelGGL((gemm_sliver_kernel<DT_F32>), grid, block, 0, stream, g, n0, nrem);
-    return hipGetLastError();
+        return launch_sliver_t<DT_BF16>(g, n0, nrem, stream);
+    if (g.ab_type == DT_F16)
+        return launch_sliver_t<DT_F16>(g, n0, nrem, stream);
+    return launch_sliver_t<DT_F32>(g, n0, nrem, stream);
 }
 
 } // namespace dg

@@ -53,8 +53,8 @@ hipError_t launch_mfma16(const GemmArgs &g, const Plan &p, hipStream_t stream);
 hipError_t launch_mfma_f32(const GemmArgs &g, const Plan &p, hipStream_t stream);
 hipError_t launch_splitk_reduce(const GemmArgs &g, const Plan &p, hipStream_t stream);
 hipError_t launch_streamk_fixup(const GemmArgs &g, const Plan &p, hipStream_t stream);
-// Columns [n0, n0 + nrem) of the output (nrem <= kMaxSliver): one
-// wavefront per row of A, row-major A with 16-byte aligned rows.
+// Columns [n0, n0 + nrem) of the output (nrem <= kMaxSliver): a few rows
+// of A per wavefront, row-major A with 16-byte aligned rows.
 constexpr int kMaxSliver = 8;
 hipError_t launch_sliver(const GemmArgs &g, int64_t n0, int32_t nrem, hipStream_t stream);
 

@@ -414,34 +414,54 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
     };
 
     // The register-loaded tile: same slots as the DMA, with the K mask (and
-    // the M / N mask on an M- or N-contiguous operand).
+    // the M / N mask on an M- or N-contiguous operand).  Every chunk's load
+    // is issued before the first LDS write, so the wave waits for memory
+    // once, not once per chunk.  With ke a multiple of 8 (uniform) no chunk
+    // straddles it: a K-contiguous chunk is then one 16-byte load from a
+    // clamped (valid) position, zeroed past ke, with no branch.
+    auto tail_chunk = [&](int i, int64_t k0, bool k_whole) -> uint4 {
+        const int q = wave * LPW + i;
+        const bool mn = from_a[i] ? AT : BT;
+        if (mn) {
+            const int cpk = from_a[i] ? A_CPK : B_CPK;
+            const int qp = from_a[i] ? q : q - A_GROUPS;
+            const int k = (64 * qp + lane) / cpk;
+            const int c = mn_slot(lane % cpk, k);
+            uint4 val = make_uint4(0u, 0u, 0u, 0u);
+            if (k0 + k < ke) {
+                const int64_t ld = from_a[i] ? lda : ldb;
+                const uint16_t *row = (from_a[i] ? A_tile : B_tile) + (k0 + k) * ld;
+                val = load_chunk_cols(row, 8 * c, from_a[i] ? a_ext : b_ext);
+            }
+            return val;
+        }
+        const int srow = q * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ swizzle_key<CPR>(srow);
+        const uint16_t *rowp = (const uint16_t *)((const char *)(from_a[i] ? A_tile : B_tile) +
+                                                  voff[i]) - c * 8;
+        const int64_t kf = k0 + c * 8;
+        if (k_whole) {
+            const uint4 x = *(const uint4 *)(rowp + (kf < ke ? kf : ke - 8));
+            return kf < ke ? x : make_uint4(0u, 0u, 0u, 0u);
+        }
+        return load_chunk_tail(rowp, kf, ke);
+    };
     auto load_tail = [&](int64_t v) {
         const int64_t k0 = tile_k0(v);
         uint4 *stage = lds + (v % kStages) * STAGE_SLOTS;
+        uint4 vals[LPW];
+        if ((ke & 7) == 0) {
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int q = wave * LPW + i;
-            const bool mn = from_a[i] ? AT : BT;
-            if (mn) {
-                const int cpk = from_a[i] ? A_CPK : B_CPK;
-                const int qp = from_a[i] ? q : q - A_GROUPS;
-                const int k = (64 * qp + lane) / cpk;
-                const int c = mn_slot(lane % cpk, k);
-                uint4 val = make_uint4(0u, 0u, 0u, 0u);
-                if (k0 + k < ke) {
-                    const int64_t ld = from_a[i] ? lda : ldb;
-                    const uint16_t *row = (from_a[i] ? A_tile : B_tile) + (k0 + k) * ld;
-                    val = load_chunk_cols(row, 8 * c, from_a[i] ? a_ext : b_ext);
-                }
-                stage[q * 64 + lane] = val;
-            } else {
-                const int srow = q * RPI + lane / CPR;
-                const int c = (lane % CPR) ^ swizzle_key<CPR>(srow);
-                const uint16_t *rowp = (const uint16_t *)((const char *)(from_a[i] ? A_tile : B_tile) +
-                                                          voff[i]) - c * 8;
-                stage[q * 64 + lane] = load_chunk_tail(rowp, k0 + c * 8, ke);
-            }
+            for (int i = 0; i < LPW; ++i)
+                vals[i] = tail_chunk(i, k0, true);
+        } else {
+#pragma unroll
+            for (int i = 0; i < LPW; ++i)
+                vals[i] = tail_chunk(i, k0, false);
         }
+#pragma unroll
+        for (int i = 0; i < LPW; ++i)
+            stage[(wave * LPW + i) * 64 + lane] = vals[i];
     };
 
     f32x16_t acc[FM][FN];
@@ -559,15 +579,17 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             fb[1][j] = frag_t{};
-        // prologue: tiles 0 .. D-1
-        for (int64_t v = 0; v < D && v < ntiles; ++v) {
-            if (v == 0 && tail)
-                load_tail(0);
-            else
+        // prologue: tiles 0 .. D-1; with a register-loaded tile 0 the DMA of
+        // tiles 1 .. D-1 goes first, so that both are in flight together
+        if (tail) {
+            for (int64_t v = 1; v < D && v < ntiles; ++v)
+                issue_dma(v);
+            load_tail(0);
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the register-path LDS writes
+        } else {
+            for (int64_t v = 0; v < D && v < ntiles; ++v)
                 issue_dma(v);
         }
-        if (tail)
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the register-path LDS writes
         int64_t v = 0;
         // steady state: D-1 later tiles stay in flight while tile v is used
         for (; v + D < ntiles; ++v) {

@@ -196,7 +196,19 @@ def sweep(p, steps, log):
     return res
 
 
-def write_table(results, path, steps, device):
+def _entry_blocks(path):
+    """The entries of an existing table file: {problem name: its three lines
+    (timings, candidates, entry)}, in file order."""
+    blocks, lines = {}, open(path).read().splitlines()
+    for i, line in enumerate(lines):
+        if line.startswith("// ") and ": heuristic " in line and i + 2 < len(lines):
+            blocks[line[3:].split(":", 1)[0]] = lines[i:i + 3]
+    return blocks
+
+
+def write_table(results, path, steps, device, keep=None):
+    """Write the table of `results`; `keep` (entry blocks of an earlier
+    table) supplies the entries of problems not swept this time."""
     lines = [
         "// Offline-tuned plans of the GEMM planner: GENERATED, do not edit.",
         f"// Made by `python3 -m dense_gemm_10_amd.tune` on {device}, "
@@ -207,7 +219,13 @@ def write_table(results, path, steps, device):
         "// slices under data-parallel, K slices per tail tile under stream-K).",
         "// Candidates: tile/schedule (dp, sk; sN for N slices) and microseconds.",
     ]
-    for r in results:
+    swept = {r["problem"].name: r for r in results}
+    order = [p.name for p in shapes() if p.name in swept or (keep and p.name in keep)]
+    for name in order:
+        if name not in swept:
+            lines.extend(keep[name])
+            continue
+        r = swept[name]
         p = r["problem"]
         tile, sched, splits, us, how = r["choice"]
         cands = ", ".join(f"{c[0].split('_', 2)[2]}/{'sk' if c[1] == 'stream_k' else 'dp'}"
@@ -226,7 +244,10 @@ def main():
     ap.add_argument("--out", default=os.path.join(HERE, "csrc", "tuned_table.inc"))
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--only", nargs="*", default=None, help="problem names to sweep")
+    ap.add_argument("--update", action="store_true",
+                    help="keep the other entries of the existing --out table")
     args = ap.parse_args()
+    keep = _entry_blocks(args.out) if args.update and os.path.exists(args.out) else None
     import torch
     if not torch.cuda.is_available():
         print("the tuning sweep needs a GPU", file=sys.stderr)
@@ -243,7 +264,7 @@ def main():
         if r is not None:
             results.append(r)
         torch.cuda.empty_cache()
-    write_table(results, args.out, args.steps, torch.cuda.get_device_name(0))
+    write_table(results, args.out, args.steps, torch.cuda.get_device_name(0), keep)
     log(f"[tune] wrote {len(results)} entries to {args.out}")
 
 
