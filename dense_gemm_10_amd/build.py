@@ -40,7 +40,8 @@ SOURCES = [
     "kernel_mfma16.hip",
     "kernel_mfma16_bf16a.hip",
     "kernel_mfma16_bf16b.hip",
-    "kernel_mfma16_f16.hip",
+    "kernel_mfma16_f16a.hip",
+    "kernel_mfma16_f16b.hip",
     "kernel_mfma16_mn256.hip",
     "kernel_mfma16_mn128.hip",
     "kernel_mfma_f32.hip",

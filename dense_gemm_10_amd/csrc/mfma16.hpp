@@ -709,13 +709,14 @@ hipError_t launch_any_layout(const GemmArgs &g, const Plan &p, hipStream_t strea
 
 } // namespace
 
-// Launchers of the instantiation files: K-contiguous bf16 tiles
-// (variants 0-4 and 5-9), K-contiguous fp16 tiles, and the M- or
+// Launchers of the instantiation files: K-contiguous bf16 and fp16 tiles
+// (variants 0-4 and 5-9 of each), and the M- or
 // N-contiguous layouts on the 256 x 256 (variant 5) and 128 x 128 (variant
 // 1) tiles of either type.
 hipError_t launch_mfma16_bf16_a(const GemmArgs &g, const Plan &p, hipStream_t stream);
 hipError_t launch_mfma16_bf16_b(const GemmArgs &g, const Plan &p, hipStream_t stream);
-hipError_t launch_mfma16_f16(const GemmArgs &g, const Plan &p, hipStream_t stream);
+hipError_t launch_mfma16_f16_a(const GemmArgs &g, const Plan &p, hipStream_t stream);
+hipError_t launch_mfma16_f16_b(const GemmArgs &g, const Plan &p, hipStream_t stream);
 hipError_t launch_mfma16_mn256(const GemmArgs &g, const Plan &p, hipStream_t stream);
 hipError_t launch_mfma16_mn128(const GemmArgs &g, const Plan &p, hipStream_t stream);
 

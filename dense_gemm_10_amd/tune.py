@@ -46,7 +46,11 @@ TILES = {
                   "mfma_bf16_256x128x32_w2x2_s3", "mfma_bf16_128x256x32_w2x2_s3",
                   "mfma_bf16_128x128x64_w2x2_s3", "mfma_bf16_256x128x64_w2x2_s3",
                   "mfma_bf16_128x256x32_w2x2_s2", "mfma_bf16_128x128x32_w2x2_s2"],
-    "mfma_f16": ["mfma_f16_256x256x64_w2x2_s2", "mfma_f16_128x128x32_w2x2_s4"],
+    "mfma_f16": ["mfma_f16_256x256x64_w2x2_s2", "mfma_f16_128x128x32_w2x2_s4",
+                 "mfma_f16_256x256x32_w2x2_s4", "mfma_f16_256x128x32_w2x2_s4",
+                 "mfma_f16_256x128x32_w2x2_s3", "mfma_f16_128x256x32_w2x2_s3",
+                 "mfma_f16_128x128x64_w2x2_s3", "mfma_f16_256x128x64_w2x2_s3",
+                 "mfma_f16_128x256x32_w2x2_s2", "mfma_f16_128x128x32_w2x2_s2"],
     "mfma_f32": ["mfma_f32_256x256x16_w2x2", "mfma_f32_128x128x16_w2x2",
                  "mfma_f32_256x256x32_w2x2", "mfma_f32_128x128x32_w2x2"],
 }

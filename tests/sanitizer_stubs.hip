@@ -10,7 +10,8 @@ namespace dg {
 
 hipError_t launch_mfma16_bf16_a(const GemmArgs &, const Plan &, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_mfma16_bf16_b(const GemmArgs &, const Plan &, hipStream_t) { return hipErrorInvalidValue; }
-hipError_t launch_mfma16_f16(const GemmArgs &, const Plan &, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_mfma16_f16_a(const GemmArgs &, const Plan &, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_mfma16_f16_b(const GemmArgs &, const Plan &, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_mfma16_mn256(const GemmArgs &, const Plan &, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_mfma16_mn128(const GemmArgs &, const Plan &, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_mfma_f32(const GemmArgs &, const Plan &, hipStream_t) { return hipErrorInvalidValue; }

@@ -195,7 +195,10 @@ def test_plans_of_the_five_workloads(monkeypatch):
     c2 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c2"]))
     assert "kernel=mfma_f32" in c2 and "programs=256" in c2
     c2v = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c2"], algo=dg.DG_ALGO_VALU_F32))
-    assert "kernel=valu_f32" in c2v and "programs=1024" in c2v
+    # 512 blocks of 128 x 256 fill the two resident blocks per CU exactly
+    assert "kernel=valu_f32" in c2v and "tile=valu_f32_128x256x16_t8x16" in c2v and "programs=512" in c2v
+    c1v = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c1"], algo=dg.DG_ALGO_VALU_F32))
+    assert "tile=valu_f32_128x128x16_t8x8" in c1v
     c3 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c3"]))
     assert "kernel=mfma_bf16" in c3 and "bm=256 bn=256" in c3 and "programs=256" in c3
     c4 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["c4"]))
@@ -231,11 +234,16 @@ def test_plans_of_the_five_workloads(monkeypatch):
     assert "schedule=data_parallel" in t4 and "sliver=1" in t4
 
 
-def test_f16_plans():
+def test_f16_plans(monkeypatch):
     f = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["f16_4096"]))
     assert "kernel=mfma_f16" in f and "tile=mfma_f16_256x256x64_w2x2_s2" in f
     g = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["f16_gelu"]))
-    assert "kernel=mfma_f16" in g and "tile=mfma_f16_128x128x32_w2x2_s4" in g
+    # the fp16 family has the bf16 family's tiles, and the tuned table uses them
+    assert "kernel=mfma_f16" in g and "tuned=1" in g and "tile=mfma_f16_" in g
+    monkeypatch.setenv("DG_TUNED", "0")
+    g0 = dg.dg_gemm_describe(_desc_for(W.WORKLOADS["f16_gelu"]))
+    assert "kernel=mfma_f16" in g0 and "tile=mfma_f16_128x128x32_w2x2_s4" in g0
+    monkeypatch.delenv("DG_TUNED")
     # every output type is accepted for 16-bit inputs
     for a in ("bf16", "f16"):
         for c in ("f32", "bf16", "f16"):

@@ -71,3 +71,36 @@ def test_every_tile(family, tile, schedule, epilogue, monkeypatch):
         ref, mag, out = oracle.gemm(p, x.A, x.B, x.C, x.bias)
         check(p, dp.result(), ref, mag, out, exact=small_int and p.act == W.ACT_NONE,
               what=f"{tile} sched={schedule} int={small_int}")
+
+
+VALU_TILES = ["valu_f32_128x128x16_t8x8", "valu_f32_128x256x16_t8x16"]
+ORDERS = [(W.ROW, W.ROW), (W.ROW, W.COL), (W.COL, W.ROW), (W.COL, W.COL)]
+
+
+@pytest.mark.parametrize("tile", VALU_TILES)
+@pytest.mark.parametrize("orders", ORDERS, ids=[f"{a}{b}" for a, b in ORDERS])
+@pytest.mark.parametrize("epilogue", ["plain", "ragged"])
+def test_every_valu_tile(tile, orders, epilogue, monkeypatch):
+    """Both thread tiles of the vector-FMA SGEMM, every operand order, on a
+    ragged grid (M = 520 and N = 600 cut the 128-row and 256-column blocks)
+    with K = 300 (a partial last K tile), checked in full."""
+    from workloads.device import DeviceProblem
+    monkeypatch.setenv("DG_FORCE_TILE", tile)
+    a_order, b_order = orders
+    base = dict(M=520, N=600, K=300, a_order=a_order, b_order=b_order, lda=None, ldb=None)
+    # the vector kernel reads 16-byte pieces: leading dimensions a multiple of 4
+    base["lda"] = 300 if a_order == W.ROW else 520
+    base["ldb"] = 600 if b_order == W.ROW else 300
+    if epilogue == "ragged":
+        base.update(alpha=1.5, beta=0.5, has_bias=True, act=W.ACT_GELU_ERF)
+    p = W.Problem(name=f"valu_{epilogue}", seed=62, **base)
+    for small_int in (True, False):
+        x = W.make_inputs(p, small_int=small_int)
+        dp = DeviceProblem(p, x, algo=dg.DG_ALGO_VALU_F32)
+        text = dp.describe()
+        print(f"[{p.name}] {text}", flush=True)
+        assert f"tile={tile} " in text
+        dp.run()
+        ref, mag, out = oracle.gemm(p, x.A, x.B, x.C, x.bias)
+        check(p, dp.result(), ref, mag, out, exact=small_int and p.act == W.ACT_NONE,
+              what=f"{tile} {a_order}{b_order} int={small_int}")
