@@ -45,6 +45,30 @@ __device__ __forceinline__ void unpack16(const uint4 q, float (&x)[VK])
                                  : half_to_f32<AB_TYPE>((uint16_t)(w[e / 2] >> (16 * (e % 2))));
 }
 
+// The 16-byte piece of row `p` (typed elements) at element k: one vector
+// load when k + VK <= kend, else element by element with zero fill past
+// kend.  `stride` is the distance between consecutive k (1, or the leading
+// dimension of a row-major B column).
+template <int AB_TYPE, int VK>
+__device__ __forceinline__ uint4 piece16(const char *p, int64_t k, int64_t stride, int64_t kend,
+                                         bool vec)
+{
+    if (vec && k + VK <= kend)
+        return *(const uint4 *)(p + k * (16 / VK));
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < VK; ++e) {
+        if (k + e < kend) {
+            const int64_t i = (k + e) * stride;
+            if (AB_TYPE == DT_F32)
+                w[e] = ((const uint32_t *)p)[i];
+            else
+                w[e / 2] |= (uint32_t)((const uint16_t *)p)[i] << (16 * (e % 2));
+        }
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // NR: columns the kernel is built for (nrem <= NR).
 template <int AB_TYPE, int NR>
 __global__ __launch_bounds__(kSliverThreads) void gemm_sliver_kernel(GemmArgs g, int64_t n0,
@@ -70,42 +94,47 @@ __global__ __launch_bounds__(kSliverThreads) void gemm_sliver_kernel(GemmArgs g,
 #pragma unroll
         for (int j = 0; j < NR; ++j)
             acc[r][j] = 0.0f;
-    for (int64_t k = (int64_t)lane * VK; k < g.K; k += 64 * VK) {
-        const bool whole = k + VK <= g.K;
-        float bv[NR][VK];
+    // kSteps K steps at a time, every load of them issued before the first
+    // FMA (kept as raw 16-byte pieces until then), so a wavefront waits for
+    // memory once per kSteps steps: for K up to 2048 16-bit elements, once
+    constexpr int kSteps = 4;
+    for (int64_t kc = (int64_t)lane * VK; kc < g.K; kc += kSteps * 64 * VK) {
+        uint4 bq[kSteps][NR], aq[kSteps][R];
 #pragma unroll
-        for (int j = 0; j < NR; ++j) {
-            const int64_t n = n0 + j;
-            if (j < nrem && b_vec && whole) {
-                unpack16<AB_TYPE, VK>(*(const uint4 *)(B + (n * g.ldb + k) * ES), bv[j]);
-            } else {
+        for (int st = 0; st < kSteps; ++st) {
+            const int64_t k = kc + (int64_t)st * 64 * VK;
 #pragma unroll
-                for (int e = 0; e < VK; ++e) {
-                    const int64_t bi = g.b_col ? n * g.ldb + k + e : (k + e) * g.ldb + n;
-                    bv[j][e] = j < nrem && k + e < g.K ? elem_f32<AB_TYPE>(B, bi) : 0.0f;
-                }
+            for (int j = 0; j < NR; ++j) {
+                const int64_t n = n0 + (j < nrem ? j : 0);
+                // column n of B: K-contiguous (b_col) or one element per row
+                const char *col = g.b_col ? B + n * g.ldb * ES : B + n * ES;
+                bq[st][j] = j < nrem ? piece16<AB_TYPE, VK>(col, k, g.b_col ? 1 : g.ldb, g.K, b_vec)
+                                     : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int64_t m = m0 + r < g.M ? m0 + r : g.M - 1;   // rows past M: any valid row, unused
+                aq[st][r] = piece16<AB_TYPE, VK>(A + m * g.lda * ES, k, 1, g.K, true);
             }
         }
-        float av[R][VK];
+        // in K order: step by step, element by element
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int64_t m = m0 + r < g.M ? m0 + r : g.M - 1;   // rows past M: any valid row, unused
-            const char *arow = A + m * g.lda * ES;
-            if (whole) {
-                unpack16<AB_TYPE, VK>(*(const uint4 *)(arow + k * ES), av[r]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < VK; ++e)
-                    av[r][e] = k + e < g.K ? elem_f32<AB_TYPE>(arow, k + e) : 0.0f;
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r)
+        for (int st = 0; st < kSteps; ++st) {
+            float bv[NR][VK];
 #pragma unroll
             for (int j = 0; j < NR; ++j)
+                unpack16<AB_TYPE, VK>(bq[st][j], bv[j]);
 #pragma unroll
-                for (int e = 0; e < VK; ++e)
-                    acc[r][j] = fmaf(av[r][e], bv[j][e], acc[r][j]);
+            for (int r = 0; r < R; ++r) {
+                float av[VK];
+                unpack16<AB_TYPE, VK>(aq[st][r], av);
+#pragma unroll
+                for (int j = 0; j < NR; ++j)
+#pragma unroll
+                    for (int e = 0; e < VK; ++e)
+                        acc[r][j] = fmaf(av[e], bv[j][e], acc[r][j]);
+            }
+        }
     }
     // sum over the wavefront's 64 lanes
 #pragma unroll

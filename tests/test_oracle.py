@@ -429,7 +429,8 @@ def test_p10_f16_rne_matches_numpy_on_random_doubles():
         np.nextafter((np.arange(1024, 2048) + 0.5) * 2.0 ** -10, 0),
         (np.arange(0, 1024) + 0.5) * 2.0 ** -24,
     ])
-    want = xs.astype(np.float16).view(np.uint16)
+    with np.errstate(over="ignore"):          # values past 65520 round to infinity on purpose
+        want = xs.astype(np.float16).view(np.uint16)
     got = np.array([oracle.round_f16(x) for x in xs], np.uint16)
     bad = np.flatnonzero(got != want)
     assert bad.size == 0, [(float.hex(float(xs[i])), hex(got[i]), hex(want[i])) for i in bad[:5]]
