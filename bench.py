@@ -272,10 +272,10 @@ def _csv_rows(outdir, suffix):
 # --warmup 5), so that a plain run and the kernel-trace pass of
 # --collect-profile time the same windows.  The chip's clock moves with its
 # power state over the first calls of a fresh process (the fp32 4096^3 call
-# falls from ~1.27 ms to ~1.0 ms over its first ~20 calls; the bf16 4096^3
-# call runs ~110 us for ~17 calls, then 125-145 us once the power limit
-# applies), so every workload also gets a second, sustained window of
-# max(K, SUSTAINED_MIN) calls after SETTLE further untimed calls.
+# takes ~1.04 ms per call over the first window and ~0.98 ms once settled;
+# the bf16 4096^3 call ~108 us, then 103-106 us), so every workload also
+# gets a second, sustained window of max(K, SUSTAINED_MIN) calls after
+# SETTLE further untimed calls.
 DEFAULT_STEPS = 20
 DEFAULT_WARMUP = 5
 SETTLE = 300
