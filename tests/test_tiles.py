@@ -104,3 +104,41 @@ def test_every_valu_tile(tile, orders, epilogue, monkeypatch):
         ref, mag, out = oracle.gemm(p, x.A, x.B, x.C, x.bias)
         check(p, dp.result(), ref, mag, out, exact=small_int and p.act == W.ACT_NONE,
               what=f"{tile} {a_order}{b_order} int={small_int}")
+
+
+RAGGED_K = [5, 13, 29, 1001]
+RAGGED_TILES = ["128x128x32_w2x2_s4", "256x256x64_w2x2_s2", "128x256x32_w2x2_s3"]
+
+
+@pytest.mark.parametrize("K", RAGGED_K)
+@pytest.mark.parametrize("tile", RAGGED_TILES)
+@pytest.mark.parametrize("dt", [W.BF16, W.F16])
+@pytest.mark.parametrize("schedule", [1, 2])
+def test_ragged_k_tail(K, tile, dt, schedule, monkeypatch):
+    """K not a multiple of 8 with leading dimensions padded to 8: the 16-bit
+    kernels' register-loaded K tail takes its element path for the chunk
+    that straddles K (a K multiple of 8 takes the clamped vector path,
+    covered by the other tile tests).  Checked in full against the oracle."""
+    from workloads.device import DeviceProblem
+    fam = "bf16" if dt == W.BF16 else "f16"
+    name = f"mfma_{fam}_{tile}"
+    monkeypatch.setenv("DG_FORCE_TILE", name)
+    up8 = (K + 7) // 8 * 8
+    p = W.Problem(name=f"raggedk{K}", M=300, N=520, K=K, a_type=dt, b_type=dt, c_type=W.F32,
+                  a_order=W.ROW, b_order=W.COL, lda=up8, ldb=up8, alpha=1.25, beta=0.5,
+                  has_bias=True, bias_type=dt, seed=63)
+    d = dg.make_desc(**dict(W.desc_fields(p), schedule=schedule))
+    try:
+        dg.dg_gemm_describe(d, 1 << 34)
+    except dg.DgError:
+        pytest.skip("no stream-K tail for this shape")
+    for small_int in (True, False):
+        x = W.make_inputs(p, small_int=small_int)
+        dp = DeviceProblem(p, x, schedule=schedule)
+        text = dp.describe()
+        print(f"[{p.name}] {text}", flush=True)
+        assert f"tile={name} " in text
+        dp.run()
+        ref, mag, out = oracle.gemm(p, x.A, x.B, x.C, x.bias)
+        check(p, dp.result(), ref, mag, out, exact=small_int,
+              what=f"{name} K={K} sched={schedule} int={small_int}")
