@@ -674,6 +674,18 @@ dg_status enqueue(const dg_gemm_desc *d, const CallPlan &cp, const void *A, cons
     const Plan &p = cp.plan;
     GemmArgs g;
     fill_args(&cp.main, p, A, B, C, ws, &g);
+    // One sliver column behind a data-parallel 16-bit plan runs inside the
+    // tiled kernel, as workgroups after its tiles: they start as the first
+    // tiles finish, within the spread of the tiles' end times, instead of
+    // as a separate kernel after the last tile (whose chain of dependent
+    // loads took 4.5 to 8 us on its own).
+    const bool fused_sliver = cp.nrem == 1 && p.splits == 1 && p.sk.tail_tiles == 0 &&
+                              (p.kernel == KERNEL_MFMA_BF16 || p.kernel == KERNEL_MFMA_F16);
+    if (fused_sliver) {
+        g.sliver_n0 = cp.main.N;
+        g.main_programs = p.programs;
+        g.sliver_blocks = ceil_div(d->M, kSliverRowsPerBlock);
+    }
     hipError_t err = hipSuccess;
     switch (p.kernel) {
     case KERNEL_GENERIC: err = launch_generic(g, p, s); break;
@@ -695,7 +707,7 @@ dg_status enqueue(const dg_gemm_desc *d, const CallPlan &cp, const void *A, cons
         if (err != hipSuccess)
             return DG_ERROR_LAUNCH;
     }
-    if (cp.nrem > 0) {
+    if (cp.nrem > 0 && !fused_sliver) {
         GemmArgs gs;
         fill_args(d, p, A, B, C, nullptr, &gs);
         err = launch_sliver(gs, cp.main.N, cp.nrem, s);

@@ -30,6 +30,12 @@ struct GemmArgs {
     SchedArgs sched;
     StreamK sk;                    // sk.tail_tiles == 0: data-parallel launch
     float *sk_parts;               // stream-K partials, [tail tile][slice][BM * BN] fp32
+    // One sliver column (output column sliver_n0) run by a tiled kernel as
+    // extra workgroups after its main_programs tile programs, with
+    // sliver_blocks (per batch entry) of rows each; 0 sliver_blocks: none.
+    int64_t sliver_n0;
+    int64_t main_programs;
+    int64_t sliver_blocks;
 };
 
 enum { ACT_NONE = 0, ACT_GELU_ERF = 1, ACT_GELU_TANH = 2 };

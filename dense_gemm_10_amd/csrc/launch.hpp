@@ -56,6 +56,9 @@ hipError_t launch_streamk_fixup(const GemmArgs &g, const Plan &p, hipStream_t st
 // Columns [n0, n0 + nrem) of the output (nrem <= kMaxSliver): a few rows
 // of A per wavefront, row-major A with 16-byte aligned rows.
 constexpr int kMaxSliver = 8;
+constexpr int kSliverThreads = 256;        // 4 wavefronts per workgroup
+constexpr int kSliverRows = 4;             // rows of A per wavefront
+constexpr int kSliverRowsPerBlock = kSliverThreads / 64 * kSliverRows;
 hipError_t launch_sliver(const GemmArgs &g, int64_t n0, int32_t nrem, hipStream_t stream);
 
 // Tile configurations of each family (defined next to the kernels).

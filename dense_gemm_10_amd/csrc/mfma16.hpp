@@ -64,6 +64,7 @@
 #pragma once
 #include "epilogue.hpp"
 #include "launch.hpp"
+#include "sliver.hpp"
 
 namespace dg {
 
@@ -658,6 +659,11 @@ __global__ __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(mfma16_per_cu(BM, BN, kStages, MBK))))
 void gemm_mfma_bf16_kernel(GemmArgs g)
 {
+    if (g.sliver_blocks && (int64_t)blockIdx.x >= g.main_programs) {
+        const int64_t i = (int64_t)blockIdx.x - g.main_programs;
+        sliver_block<DT_BF16, 1>(g, g.sliver_n0, 1, i % g.sliver_blocks, i / g.sliver_blocks);
+        return;
+    }
     extern __shared__ uint4 lds[];
     mfma16_program<DT_BF16, BM, BN, WM, WN, kStages, MBK, AT, BT>(g, lds);
 }
@@ -667,6 +673,11 @@ __global__ __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(mfma16_per_cu(BM, BN, kStages, MBK))))
 void gemm_mfma_f16_kernel(GemmArgs g)
 {
+    if (g.sliver_blocks && (int64_t)blockIdx.x >= g.main_programs) {
+        const int64_t i = (int64_t)blockIdx.x - g.main_programs;
+        sliver_block<DT_F16, 1>(g, g.sliver_n0, 1, i % g.sliver_blocks, i / g.sliver_blocks);
+        return;
+    }
     extern __shared__ uint4 lds[];
     mfma16_program<DT_F16, BM, BN, WM, WN, kStages, MBK, AT, BT>(g, lds);
 }
@@ -675,7 +686,9 @@ template <int T, int BM, int BN, int WM, int WN, int NS, int BK, bool AT, bool B
 hipError_t launch_layout(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
     const size_t lds_bytes = (size_t)mfma16_lds_bytes(BM, BN, NS, BK);
-    const dim3 grid((unsigned)p.programs), block(64 * WM * WN);
+    static_assert(64 * WM * WN == kSliverThreads, "sliver workgroups share the kernel's block");
+    const int64_t programs = p.programs + g.sliver_blocks * g.sched.batch;
+    const dim3 grid((unsigned)programs), block(64 * WM * WN);
     if constexpr (T == DT_F16)
         hipLaunchKernelGGL((gemm_mfma_f16_kernel<BM, BN, WM, WN, NS, BK, AT, BT>), grid, block,
                            lds_bytes, stream, g);
