@@ -313,13 +313,21 @@ def _timed_means(out, warmup, steps, settle):
     return res
 
 
+def _is_gemm(kernel_name):
+    """A call's dominant kernel: the tiled (or generic / vector) GEMM, not
+    the stand-alone sliver kernel some plans launch after it."""
+    return "gemm_" in kernel_name and "gemm_sliver" not in kernel_name
+
+
 def _per_dispatch(rows, name_filter):
     """Mean over dispatches of the per-dispatch sum (over instances) of the
-    counter, for kernels whose name contains name_filter."""
+    counter, for kernels whose name contains name_filter ("gemm_": the
+    call's GEMM kernel, see _is_gemm)."""
     import collections
     per = collections.defaultdict(float)
     for r in rows:
-        if name_filter in r["Kernel_Name"]:
+        name = r["Kernel_Name"]
+        if (_is_gemm(name) if name_filter == "gemm_" else name_filter in name):
             per[r["Dispatch_Id"]] += float(r["Counter_Value"])
     if not per:
         raise RuntimeError(f"no dispatch of a kernel matching {name_filter!r}")
@@ -410,7 +418,7 @@ def collect_profile(workload, tmp, out_dir=PROFILES, knobs=(), steps=DEFAULT_STE
     cmd = _rocprof(["--pmc", "GRBM_GUI_ACTIVE"], out) + child + short
     log(f"[profile] {' '.join(cmd)}")
     subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL)
-    rows = [r for r in _csv_rows(out, "counter_collection.csv") if "gemm_" in r["Kernel_Name"]]
+    rows = [r for r in _csv_rows(out, "counter_collection.csv") if _is_gemm(r["Kernel_Name"])]
     clocks = []
     for r in rows:
         try:
@@ -700,7 +708,7 @@ def run_ablation(steps, settle, tmp, out_dir=PROFILES):
         log(f"[ablation] {' '.join(cmd)}")
         subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL)
         cmds[name] = _shown(cmd, tmp)
-        rows = [r for r in _csv_rows(out, "counter_collection.csv") if "gemm_" in r["Kernel_Name"]]
+        rows = [r for r in _csv_rows(out, "counter_collection.csv") if _is_gemm(r["Kernel_Name"])]
         for cn in pmc:
             per = {}
             for r in rows:
