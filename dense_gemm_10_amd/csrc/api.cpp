@@ -28,14 +28,12 @@ namespace {
 
 constexpr int64_t kNumCu = 256;          // MI355X compute units
 // Group height of the grouped tile order ("GEMM Kernel Optimization", L2
-// Cache Grouping, which starts from 8).  Measured over G = 1, 4, 8, 16 with
-// and without the XCD remap at 4096^3 (fp32, bf16) and 8192^3 (bf16): the
-// orders change the fetched bytes up to 2.75x at 8192^3, and the time there
-// by up to 6 % on one box (block-forming orders 759-762 us, strips 806-808
-// us) and 1 % on another; at 4096^3 every order runs within 3 %.  4 with
-// the remap gives each XCD's 32 concurrent tiles a 4 x 8 block (the fewest
-// misses) and was within 0.5 % of the fastest order at every size in both
-// runs.
+// Cache Grouping, which starts from 8).  4 with the XCD remap gives each
+// XCD's 32 concurrent 256 x 256 tiles a 4 x 8 block of the tile grid: the
+// fewest A and B panels, so the fewest L2 misses, of the group heights 1,
+// 4, 8 and 16 with and without the remap.  The tile-order ablation
+// (bench.py --ablation) measures the misses and the time of each order at
+// 4096^3 and 8192^3.
 constexpr int32_t kDefaultGroupM = 4;
 constexpr int32_t kMaxSplits = 256;
 
