@@ -612,7 +612,7 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
     // the epilogue keeps within the kernel's register budget
     constexpr int REGS = 512 / mfma16_per_cu(BM, BN, kStages, MBK);
     if (part)
-        tile_epilogue_rows<BM, BN, WM, WN, true, DT_F32, REGS>(g, (char *)part, BN, BM, BN, n0,
+        tile_epilogue_rows<BM, BN, WM, WN, true, DT_F32, REGS, false>(g, (char *)part, BN, BM, BN, n0,
                                                                (float *)lds, acc);
     else
         tile_epilogue<BM, BN, WM, WN, REGS>(g, tc, (float *)lds, m0, n0, acc);
