@@ -187,9 +187,33 @@ __global__ __launch_bounds__(256) void splitk_reduce4_kernel(GemmArgs g, int32_t
         const uint32_t row = e / N, n = e - row * N;
         const uint32_t b = row / M, m = row - b * M;
         const float acc[4] = {sum.x, sum.y, sum.z, sum.w};
+        float v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            store_c(g, b, m, n + j, epilogue_value(g, b, m, n + j, acc[j]));
+            v[j] = epilogue_value(g, b, m, n + j, acc[j]);
+        // the four outputs are consecutive in a row-major C: one aligned
+        // 8-byte (16-bit C) or 16-byte (fp32 C) non-temporal store
+        const int64_t ci = (int64_t)b * g.sc + (int64_t)m * g.ldc + n;
+        const int es = g.c_type == DT_F32 ? 4 : 2;
+        char *dst = (char *)g.C + ci * es;
+        if (!g.c_col && ((uintptr_t)dst & (uintptr_t)(4 * es - 1)) == 0) {
+            if (g.c_type == DT_F32) {
+                typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store((f32x4_nt){v[0], v[1], v[2], v[3]}, (f32x4_nt *)dst);
+            } else {
+                typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));
+                uint32_t h[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    h[j] = g.c_type == DT_F16 ? f32_to_f16(v[j]) : f32_to_bf16(v[j]);
+                __builtin_nontemporal_store((u32x2_nt){h[0] | (h[1] << 16), h[2] | (h[3] << 16)},
+                                            (u32x2_nt *)dst);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                store_c(g, b, m, n + j, v[j]);
+        }
     }
 }
 
