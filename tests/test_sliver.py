@@ -58,6 +58,15 @@ CASES = [
     W.Problem(name="sliver_colmajor_c", M=4096, N=4096 + 1, K=100, lda=112, ldb=104,
               a_type=W.BF16, b_type=W.BF16, c_type=W.F32, a_order=W.ROW, b_order=W.COL,
               c_order=W.COL, alpha=1.0, beta=0.0, seed=94),
+    # one column behind a data-parallel 16-bit plan runs inside the tiled
+    # kernel (workgroups after its tiles, batch entry from the program id):
+    # batched with B broadcast, and a row-major bf16 output with GELU
+    W.Problem(name="sliver_inside_f16_batch", M=2048, N=2048 + 1, K=128, batch=4, a_type=W.F16,
+              b_type=W.F16, c_type=W.F16, a_order=W.ROW, b_order=W.COL, stride_b=0,
+              alpha=1.0, beta=0.25, has_bias=True, bias_type=W.F16, seed=95),
+    W.Problem(name="sliver_inside_bf16_gelu", M=4096, N=4096 + 1, K=200, a_type=W.BF16,
+              b_type=W.BF16, c_type=W.BF16, a_order=W.ROW, b_order=W.COL, has_bias=True,
+              bias_type=W.BF16, act=W.ACT_GELU_ERF, seed=96),
 ]
 
 
