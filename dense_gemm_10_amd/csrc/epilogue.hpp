@@ -158,16 +158,24 @@ constexpr int kEpilogueRows = 64;
 constexpr int epilogue_ld(int BN) { return BN + 8; }
 constexpr int epilogue_lds_bytes(int BN) { return (kEpilogueRows * epilogue_ld(BN) + BN) * 4; }
 
+// The epilogue reads a wave's accumulators as FM x FN 32 x 32 blocks in the
+// 32 x 32 MFMA register layout, one block at a time through acc_block; a
+// kernel that accumulates in another layout passes a view type with its
+// own acc_block overload (found by argument-dependent lookup).
+template <int FM, int FN>
+__device__ __forceinline__ const f32x16_t &acc_block(const f32x16_t (&acc)[FM][FN], int i, int j)
+{
+    return acc[i][j];
+}
+
 // Accumulator blocks of rows [c * EP_ROWS, (c + 1) * EP_ROWS) of the tile into
 // the LDS chunk (fp32, row stride EP_LD).  Lane l's value v of a 32 x 32
 // block is row 8*(v/4) + 4*(l/32) + v%4, column l%32 of that block; wave
 // (wm, wn) owns blocks FM x FN at rows wm*TM + 32i, columns wn*TN + 32j.
 // Tile row r is stored shifted right by shift(r) < 8 floats (0 for the
 // generic path), with EP_LD leaving room for it.
-template <int BM, int BN, int WM, int WN, typename Shift>
-__device__ __forceinline__ void stage_chunk(float *chunk, int c,
-                                            const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32],
-                                            Shift shift)
+template <int BM, int BN, int WM, int WN, typename Shift, typename ACC>
+__device__ __forceinline__ void stage_chunk(float *chunk, int c, const ACC &acc, Shift shift)
 {
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
@@ -180,12 +188,14 @@ __device__ __forceinline__ void stage_chunk(float *chunk, int c,
         const int row0 = wm * TM + i * 32 - c * EP_ROWS;   // block's first row in the chunk
         if (row0 >= 0 && row0 < EP_ROWS) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = row0 + 8 * (v / 4) + 4 * frag_half + (v % 4);
-                float *dst = chunk + row * EP_LD + shift(c * EP_ROWS + row) + wn * TN + (lane & 31);
+            for (int j = 0; j < FN; ++j) {
+                const f32x16_t blk = acc_block(acc, i, j);
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    dst[j * 32] = acc[i][j][v];
+                for (int v = 0; v < 16; ++v) {
+                    const int row = row0 + 8 * (v / 4) + 4 * frag_half + (v % 4);
+                    chunk[row * EP_LD + shift(c * EP_ROWS + row) + wn * TN + (lane & 31) + j * 32] =
+                        blk[v];
+                }
             }
         }
     }
@@ -220,10 +230,10 @@ __device__ __forceinline__ void static_for(F &&f)
 // a partial tail block: slot js takes full block js + 1 (the last slot has
 // none), and a pass per chunk stores the head and tail elements one by one.
 template <int BM, int BN, int WM, int WN, bool PARTIAL, int OUT, int REGS, bool SHIFTED,
-          bool STREAM = true>
+          bool STREAM = true, typename ACC>
 __device__ __forceinline__ void tile_epilogue_whole(const GemmArgs &g, char *out, int64_t ld,
                                                     int64_t n0, float *lds, int d0, int dl,
-                                                    const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
+                                                    const ACC &acc)
 {
     constexpr int NT = 64 * WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -286,13 +296,14 @@ __device__ __forceinline__ void tile_epilogue_whole(const GemmArgs &g, char *out
     // each shifted by its tile row's misalignment.
     auto stage = [&](auto I) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int rb = 8 * (v / 4) + 4 * frag_half + (v % 4);
-            float *dst = lds + (wm * 32 + rb) * EP_LD + shift(wm * TM + decltype(I)::value * 32 + rb) +
-                         wn * TN + (lane & 31);
+        for (int j = 0; j < FN; ++j) {
+            const f32x16_t blk = acc_block(acc, decltype(I)::value, j);
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                dst[j * 32] = acc[decltype(I)::value][j][v];
+            for (int v = 0; v < 16; ++v) {
+                const int rb = 8 * (v / 4) + 4 * frag_half + (v % 4);
+                lds[(wm * 32 + rb) * EP_LD + shift(wm * TM + decltype(I)::value * 32 + rb) +
+                    wn * TN + (lane & 31) + j * 32] = blk[v];
+            }
         }
     };
     // alpha, beta * C, bias and activation of one value at tile column col
@@ -456,10 +467,10 @@ __device__ __forceinline__ void tile_epilogue_whole(const GemmArgs &g, char *out
 // stride (elements), rows x cols the part of the tile inside the output and
 // n0 the tile's first column (for the bias).
 template <int BM, int BN, int WM, int WN, bool PARTIAL, int OUT, int REGS = 512,
-          bool STREAM = true>
+          bool STREAM = true, typename ACC>
 __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out, int64_t ld,
                                                    int rows, int cols, int64_t n0, float *lds,
-                                                   const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
+                                                   const ACC &acc)
 {
     constexpr int NT = 64 * WM * WN;
     constexpr int EP_ROWS = kEpilogueRows, EP_LD = epilogue_ld(BN);
@@ -582,10 +593,9 @@ __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out,
 // bytes and no wave may still be reading it for other purposes.  Row-major
 // outputs (and split-K partials) take tile_epilogue_rows; a column-major C
 // goes through store_chunk.
-template <int BM, int BN, int WM, int WN, int REGS = 512>
+template <int BM, int BN, int WM, int WN, int REGS = 512, typename ACC>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs &g, const TileCoord &tc, float *lds,
-                                              int64_t m0, int64_t n0,
-                                              const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
+                                              int64_t m0, int64_t n0, const ACC &acc)
 {
     const int rows = (int)(g.M - m0 < BM ? g.M - m0 : BM);
     const int cols = (int)(g.N - n0 < BN ? g.N - n0 : BN);

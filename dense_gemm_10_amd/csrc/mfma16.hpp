@@ -4,9 +4,11 @@
 // the dispatch.
 //
 // bf16 and fp16 GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16 and
-// its fp16 twin v_mfma_f32_32x32x16_f16), fp32 accumulation.  The two
-// element types share every byte of the data path (loads, LDS layout,
-// fragments, epilogue); only the MFMA instruction differs.
+// its fp16 twin v_mfma_f32_32x32x16_f16; the 256 x 256 tile of K-contiguous
+// operands uses the 16 x 16 x 32 shapes, see mfma_16x16x32), fp32
+// accumulation.  The two element types share every byte of the data path
+// (loads, LDS layout, fragments, epilogue); only the MFMA instruction
+// differs.
 //
 // The structure is the tiled blocked GEMM of "GEMM Kernel Optimization"
 // (Core Technique: one workgroup per BM x BN output tile, K walked in
@@ -42,9 +44,10 @@
 //     bank groups.  The DMA lanes are assigned so that consecutive lanes
 //     fill consecutive slots: lane l loads the global chunk that belongs in
 //     slot l.
-//   LDS -> registers: ds_read_b128 fragments, BK / 16 k-steps per stage;
+//   LDS -> registers: ds_read_b128 fragments, BK / 16 (BK / 32 with 16 x 16
+//     blocks) k-steps per stage;
 //   MFMA: each wavefront owns a TM x TN wave tile = FM x FN blocks of
-//     32 x 32, accumulated in FM*FN*16 fp32 registers per lane.
+//     32 x 32 (or 16 x 16), accumulated in TM*TN/64 fp32 registers per lane.
 // The DMA is issued through inline assembly so that the compiler does not
 // serialise it: vector-memory loads of a wave complete in order, so waiting
 // until at most (NSTAGE - 2) tiles' loads are outstanding (s_waitcnt
@@ -85,6 +88,82 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(bf16x8_t a, bf16x8_t b, f32x16
 __device__ __forceinline__ f32x16_t mfma_32x32x16(f16x8_t a, f16x8_t b, f32x16_t c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// The 16 x 16 x 32 shape: lane l holds A row l mod 16 (B column l mod 16),
+// k = 8 (l / 16) .. + 7, and accumulates rows 4 (l / 16) .. + 3 of column
+// l mod 16.  Under the chip's power limit it sustains about 13 % more
+// than the 32 x 32 x 16 shape on the same data (a probe of both shapes fed
+// from LDS: 1.64 against 1.45 PFLOP/s): half the accumulator register
+// traffic per flop.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32(f16x8_t a, f16x8_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Accumulators of one MFMA block: 32 x 32 (16 per lane) or 16 x 16 (4).
+template <int MS> struct acc_of { using type = f32x16_t; };
+template <> struct acc_of<16> { using type = f32x4_t; };
+
+template <typename F>
+__device__ __forceinline__ f32x16_t mfma_block(F a, F b, f32x16_t c) { return mfma_32x32x16(a, b, c); }
+template <typename F>
+__device__ __forceinline__ f32x4_t mfma_block(F a, F b, f32x4_t c) { return mfma_16x16x32(a, b, c); }
+
+// Four 16 x 16 accumulator blocks (rows 16 bi, columns 16 bj of a 32 x 32
+// block) rearranged into the 32 x 32 block's register layout (lane l,
+// value v: row 8 (v / 4) + 4 (l / 32) + v mod 4, column l mod 32), which the
+// epilogue reads.  Value v of lane 16 g + c in block (bi, bj) is row
+// 16 bi + 4 g + v, column 16 bj + c; it belongs in lane 32 (g mod 2) +
+// 16 bj + c, value 8 bi + 4 (g / 2) + v.  Per (bi, v) that is, in 16-lane
+// groups, [X0 X1 X2 X3], [Y0 Y1 Y2 Y3] (bj = 0, 1) -> [X0 Y0 X1 Y1],
+// [X2 Y2 X3 Y3]: a swap of odd groups of X with even groups of Y
+// (v_permlane16_swap), then of the upper half of the first result with
+// the lower half of the second (v_permlane32_swap), lane layouts measured
+// on gfx950.  Both instructions rewrite both of their registers; they are
+// written as assembly on two in-out operands because the compiler's
+// two-result builtins, chained, dropped the second result (both outputs
+// came back equal); not volatile, so that the compiler can place each
+// group's swaps next to the epilogue's use of it.  The s_nop keeps a VALU
+// write of either register two wait states away from the swap that reads
+// it.
+__device__ __forceinline__ f32x16_t acc16_to_32(const f32x4_t &b00, const f32x4_t &b01,
+                                                const f32x4_t &b10, const f32x4_t &b11)
+{
+    f32x16_t r;
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float x = bi ? b10[v] : b00[v], y = bi ? b11[v] : b01[v];
+            asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\t"
+                "s_nop 1\n\tv_permlane32_swap_b32 %0, %1"
+                : "+v"(x), "+v"(y));
+            r[8 * bi + v] = x;
+            r[8 * bi + 4 + v] = y;
+        }
+    return r;
+}
+
+// A wave's FM x FN 16 x 16 accumulator blocks seen by the epilogue as
+// (FM / 2) x (FN / 2) 32 x 32 blocks.
+template <int FM, int FN>
+struct Acc16View {
+    const f32x4_t (&a)[FM][FN];
+};
+
+template <int FM, int FN>
+__device__ __forceinline__ f32x16_t acc_block(const Acc16View<FM, FN> &v, int i, int j)
+{
+    return acc16_to_32(v.a[2 * i][2 * j], v.a[2 * i][2 * j + 1], v.a[2 * i + 1][2 * j],
+                       v.a[2 * i + 1][2 * j + 1]);
 }
 
 
@@ -283,7 +362,8 @@ __device__ __forceinline__ frag_t tr_fragment(uint32_t addr0)
 // past the edge, inside the leading dimension for every k-row but the
 // matrix's last, so a K range that ends at K loads its last K tile through
 // registers with both masks.
-template <int T, int BM, int BN, int WM, int WN, int kStages, int MBK, bool AT, bool BT>
+template <int T, int BM, int BN, int WM, int WN, int kStages, int MBK, bool AT, bool BT,
+          int MS = 32>
 __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int64_t kb,
                                             int64_t ke, float *part, uint4 *lds)
 {
@@ -291,9 +371,15 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
     constexpr int NT = 64 * WM * WN;
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;    // wave tile
-    constexpr int FM = TM / 32, FN = TN / 32;    // 32x32 blocks per wave
+    constexpr int FM = TM / MS, FN = TN / MS;    // MS x MS MFMA blocks per wave
+    constexpr int KD = MS == 32 ? 16 : 32;       // k of one MFMA
+    constexpr int CPS = KD / 8;                  // 16-byte chunks of a fragment row per k-step
     constexpr int CPR = MBK / 8;                 // 16-byte chunks per stage row
-    constexpr int KS = MBK / 16;                 // MFMA k-steps per stage
+    constexpr int KS = MBK / KD;                 // MFMA k-steps per stage
+    using acc_t = typename acc_of<MS>::type;
+    constexpr int NV = MS == 32 ? 16 : 4;        // accumulators per lane per block
+    static_assert(MS == 32 || (MS == 16 && !AT && !BT),
+                  "16 x 16 blocks read K-contiguous operands only");
     constexpr int RPI = 64 / CPR;                // stage rows per DMA instruction
     constexpr int ROWS = BM + BN;                // stage rows: A rows, then B columns
     constexpr int GROUPS = ROWS / RPI;           // DMA instructions per stage
@@ -399,13 +485,12 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
     // DMA instruction i (of LPW) of full tile v into its stage.
     auto issue_dma_one = [&](int64_t v, int i) {
         const int64_t k0 = tile_k0(v);
-        const uint32_t stage_addr = lds_base + (uint32_t)((v % kStages) * STAGE_SLOTS * 16);
-        const int q = wave * LPW + i;
+        const uint32_t dst = lds_base + (uint32_t)((v % kStages) * STAGE_SLOTS * 16) +
+                             (uint32_t)((wave * LPW + i) * 1024);
 #ifdef DG_LOAD_POLICY
-        dma_16_policy(from_a[i], uniform_ptr(group_base(i, k0)), voff[i],
-                      stage_addr + (uint32_t)(q * 64 * 16));
+        dma_16_policy(from_a[i], uniform_ptr(group_base(i, k0)), voff[i], dst);
 #else
-        dma_16(uniform_ptr(group_base(i, k0)), voff[i], stage_addr + (uint32_t)(q * 64 * 16));
+        dma_16(uniform_ptr(group_base(i, k0)), voff[i], dst);
 #endif
     };
     auto issue_dma = [&](int64_t v) {
@@ -449,7 +534,6 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
     };
     auto load_tail = [&](int64_t v) {
         const int64_t k0 = tile_k0(v);
-        uint4 *stage = lds + (v % kStages) * STAGE_SLOTS;
         uint4 vals[LPW];
         if ((ke & 7) == 0) {
 #pragma unroll
@@ -462,20 +546,20 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
         }
 #pragma unroll
         for (int i = 0; i < LPW; ++i)
-            stage[(wave * LPW + i) * 64 + lane] = vals[i];
+            lds[(v % kStages) * STAGE_SLOTS + (wave * LPW + i) * 64 + lane] = vals[i];
     };
 
-    f32x16_t acc[FM][FN];
+    acc_t acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
+            for (int v = 0; v < NV; ++v)
                 acc[i][j][v] = 0.0f;
 
-    const int frag_row = lane & 31;       // row of A / column of B this lane feeds
-    const int frag_half = lane >> 5;      // which 8 of the 16 k of one MFMA step
+    const int frag_row = lane % MS;       // row of A / column of B this lane feeds
+    const int frag_grp = lane / MS;       // which 8 of the KD k of one MFMA step
     const int swz = swizzle_key<CPR>(frag_row);   // key of every fragment row (period 16)
     // Transposing reads: lane 16g + 4r + q addresses k-row 8 (g / 2) + r of
     // a k-step and columns 16 (g mod 2) + 4q .. + 3 of a fragment (see
@@ -495,7 +579,7 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
     if constexpr (BT) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            b_tr[j] = (uint32_t)(BM * MBK * 2 + tr_krow * BN * 2 +
+            b_tr[j] = (uint32_t)(tr_krow * BN * 2 +
                                  16 * mn_slot((wn * TN + 32 * j) / 8 + tr_chunk, tr_krow) +
                                  8 * (tr_q & 1));
     }
@@ -505,7 +589,7 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                acc[i][j] = mfma_32x32x16(af[i], bf[j], acc[i][j]);
+                acc[i][j] = mfma_block(af[i], bf[j], acc[i][j]);
     };
 
     // Two fragment register sets, alternating per k-step; fa[1]/fb[1]
@@ -530,34 +614,34 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
     constexpr int DMA_WINDOW = DMA_STEPS * FM * FN;
     constexpr int MFMA_PER_DMA = DMA_WINDOW / LPW > 0 ? DMA_WINDOW / LPW : 1;
     static_assert(FM + FN <= FM * FN, "fragment reads fit in the slots");
-    auto stage_body = [&](int st, bool dma, int64_t v_dma) {
-        const uint4 *as = lds + st * STAGE_SLOTS + (wm * TM + frag_row) * CPR;
-        const uint4 *bs = lds + st * STAGE_SLOTS + (BM + wn * TN + frag_row) * CPR;
-        const uint32_t st_addr = lds_base + (uint32_t)(st * STAGE_SLOTS * 16);
+    // a_off / b_off: LDS byte offsets of A's and B's part of the stage;
+    // issue(d) runs after the MFMA of slot d (DMA of later tiles).
+    auto stage_body = [&](uint32_t a_off, uint32_t b_off, auto &&issue) {
+        const uint4 *as = lds + a_off / 16 + (wm * TM + frag_row) * CPR;
+        const uint4 *bs = lds + b_off / 16 + (wn * TN + frag_row) * CPR;
+        const uint32_t a_addr = lds_base + a_off, b_addr = lds_base + b_off;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int cur = ks & 1, prev = cur ^ 1;
-            const int c = (ks * 2 + frag_half) ^ swz;
+            const int c = (ks * CPS + frag_grp) ^ swz;
 #pragma unroll
             for (int n = 0; n < FM * FN; ++n) {
                 if (n < FM) {
                     if constexpr (AT)
-                        fa[cur][n] = tr_fragment<frag_t, BM * 2>(st_addr + a_tr[n] +
+                        fa[cur][n] = tr_fragment<frag_t, BM * 2>(a_addr + a_tr[n] +
                                                                   16 * ks * BM * 2);
                     else
-                        fa[cur][n] = __builtin_bit_cast(frag_t, as[n * 32 * CPR + c]);
+                        fa[cur][n] = __builtin_bit_cast(frag_t, as[n * MS * CPR + c]);
                 } else if (n < FM + FN) {
                     if constexpr (BT)
-                        fb[cur][n - FM] = tr_fragment<frag_t, BN * 2>(st_addr + b_tr[n - FM] +
+                        fb[cur][n - FM] = tr_fragment<frag_t, BN * 2>(b_addr + b_tr[n - FM] +
                                                                        16 * ks * BN * 2);
                     else
-                        fb[cur][n - FM] = __builtin_bit_cast(frag_t, bs[(n - FM) * 32 * CPR + c]);
+                        fb[cur][n - FM] = __builtin_bit_cast(frag_t, bs[(n - FM) * MS * CPR + c]);
                 }
                 const int i = n / FN, j = n % FN;
-                acc[i][j] = mfma_32x32x16(fa[prev][i], fb[prev][j], acc[i][j]);
-                const int d = ks * FM * FN + n;
-                if (dma && (d % MFMA_PER_DMA) == MFMA_PER_DMA - 1 && d / MFMA_PER_DMA < LPW)
-                    issue_dma_one(v_dma, d / MFMA_PER_DMA);
+                acc[i][j] = mfma_block(fa[prev][i], fb[prev][j], acc[i][j]);
+                issue(ks * FM * FN + n);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -580,6 +664,7 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             fb[1][j] = frag_t{};
+        auto no_dma = [](int) {};
         // prologue: tiles 0 .. D-1; with a register-loaded tile 0 the DMA of
         // tiles 1 .. D-1 goes first, so that both are in flight together
         if (tail) {
@@ -591,18 +676,25 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
             for (int64_t v = 0; v < D && v < ntiles; ++v)
                 issue_dma(v);
         }
+        auto stage_off = [](int64_t v) -> uint32_t {
+            return (uint32_t)((v % kStages) * STAGE_SLOTS * 16);
+        };
+        constexpr uint32_t B_OFF = (uint32_t)BM * MBK * 2;   // B's rows follow A's
         int64_t v = 0;
         // steady state: D-1 later tiles stay in flight while tile v is used
         for (; v + D < ntiles; ++v) {
             __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm((D - 1) * LPW));
             barrier();
-            stage_body((int)(v % kStages), true, v + D);
+            stage_body(stage_off(v), stage_off(v) + B_OFF, [&](int d) {
+                if (d % MFMA_PER_DMA == MFMA_PER_DMA - 1 && d / MFMA_PER_DMA < LPW)
+                    issue_dma_one(v + D, d / MFMA_PER_DMA);
+            });
         }
         // drain
         for (; v < ntiles; ++v) {
             __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
             barrier();
-            stage_body((int)(v % kStages), false, 0);
+            stage_body(stage_off(v), stage_off(v) + B_OFF, no_dma);
         }
         mfma_step(fa[1], fb[1]);   // last k-step of the last stage
         __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
@@ -611,18 +703,29 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
 
     // the epilogue keeps within the kernel's register budget
     constexpr int REGS = 512 / mfma16_per_cu(BM, BN, kStages, MBK);
-    if (part)
-        tile_epilogue_rows<BM, BN, WM, WN, true, DT_F32, REGS, false>(g, (char *)part, BN, BM, BN, n0,
-                                                               (float *)lds, acc);
-    else
-        tile_epilogue<BM, BN, WM, WN, REGS>(g, tc, (float *)lds, m0, n0, acc);
+    if constexpr (MS == 32) {
+        if (part)
+            tile_epilogue_rows<BM, BN, WM, WN, true, DT_F32, REGS, false>(
+                g, (char *)part, BN, BM, BN, n0, (float *)lds, acc);
+        else
+            tile_epilogue<BM, BN, WM, WN, REGS>(g, tc, (float *)lds, m0, n0, acc);
+    } else {
+        // the epilogue reads 32 x 32 blocks, each rearranged from a 2 x 2
+        // group of 16 x 16 blocks where it is staged
+        const Acc16View<FM, FN> view{acc};
+        if (part)
+            tile_epilogue_rows<BM, BN, WM, WN, true, DT_F32, REGS, false>(
+                g, (char *)part, BN, BM, BN, n0, (float *)lds, view);
+        else
+            tile_epilogue<BM, BN, WM, WN, REGS>(g, tc, (float *)lds, m0, n0, view);
+    }
 }
 
 // Data-parallel launches give each program one tile (or split-K slice).
 // Stream-K launches give programs [0, dp_tiles) one whole tile each and the
 // others one K slice of a tail tile, written as a raw fp32 partial that the
 // fix-up kernel adds up.
-template <int T, int BM, int BN, int WM, int WN, int kStages, int MBK, bool AT, bool BT>
+template <int T, int BM, int BN, int WM, int WN, int kStages, int MBK, bool AT, bool BT, int MS>
 __device__ __forceinline__ void mfma16_program(const GemmArgs &g, uint4 *lds)
 {
     const StreamK &sk = g.sk;
@@ -648,13 +751,13 @@ __device__ __forceinline__ void mfma16_program(const GemmArgs &g, uint4 *lds)
         ke = kb + sk.k_per_split < g.K ? kb + sk.k_per_split : g.K;
         part = g.sk_parts + (r * sk.tail_splits + slice) * (int64_t)(BM * BN);
     }
-    mfma16_tile<T, BM, BN, WM, WN, kStages, MBK, AT, BT>(g, tc, kb, ke, part, lds);
+    mfma16_tile<T, BM, BN, WM, WN, kStages, MBK, AT, BT, MS>(g, tc, kb, ke, part, lds);
 }
 
 // One kernel name per element type, so that traces tell them apart.  AT /
 // BT: A stored M-contiguous (column-major) / B stored N-contiguous
 // (row-major).
-template <int BM, int BN, int WM, int WN, int kStages, int MBK, bool AT, bool BT>
+template <int BM, int BN, int WM, int WN, int kStages, int MBK, bool AT, bool BT, int MS>
 __global__ __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(mfma16_per_cu(BM, BN, kStages, MBK))))
 void gemm_mfma_bf16_kernel(GemmArgs g)
@@ -665,10 +768,10 @@ void gemm_mfma_bf16_kernel(GemmArgs g)
         return;
     }
     extern __shared__ uint4 lds[];
-    mfma16_program<DT_BF16, BM, BN, WM, WN, kStages, MBK, AT, BT>(g, lds);
+    mfma16_program<DT_BF16, BM, BN, WM, WN, kStages, MBK, AT, BT, MS>(g, lds);
 }
 
-template <int BM, int BN, int WM, int WN, int kStages, int MBK, bool AT, bool BT>
+template <int BM, int BN, int WM, int WN, int kStages, int MBK, bool AT, bool BT, int MS>
 __global__ __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu(mfma16_per_cu(BM, BN, kStages, MBK))))
 void gemm_mfma_f16_kernel(GemmArgs g)
@@ -679,10 +782,10 @@ void gemm_mfma_f16_kernel(GemmArgs g)
         return;
     }
     extern __shared__ uint4 lds[];
-    mfma16_program<DT_F16, BM, BN, WM, WN, kStages, MBK, AT, BT>(g, lds);
+    mfma16_program<DT_F16, BM, BN, WM, WN, kStages, MBK, AT, BT, MS>(g, lds);
 }
 
-template <int T, int BM, int BN, int WM, int WN, int NS, int BK, bool AT, bool BT>
+template <int T, int BM, int BN, int WM, int WN, int NS, int BK, bool AT, bool BT, int MS = 32>
 hipError_t launch_layout(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
     const size_t lds_bytes = (size_t)mfma16_lds_bytes(BM, BN, NS, BK);
@@ -690,10 +793,10 @@ hipError_t launch_layout(const GemmArgs &g, const Plan &p, hipStream_t stream)
     const int64_t programs = p.programs + g.sliver_blocks * g.sched.batch;
     const dim3 grid((unsigned)programs), block(64 * WM * WN);
     if constexpr (T == DT_F16)
-        hipLaunchKernelGGL((gemm_mfma_f16_kernel<BM, BN, WM, WN, NS, BK, AT, BT>), grid, block,
+        hipLaunchKernelGGL((gemm_mfma_f16_kernel<BM, BN, WM, WN, NS, BK, AT, BT, MS>), grid, block,
                            lds_bytes, stream, g);
     else
-        hipLaunchKernelGGL((gemm_mfma_bf16_kernel<BM, BN, WM, WN, NS, BK, AT, BT>), grid, block,
+        hipLaunchKernelGGL((gemm_mfma_bf16_kernel<BM, BN, WM, WN, NS, BK, AT, BT, MS>), grid, block,
                            lds_bytes, stream, g);
     return hipGetLastError();
 }
@@ -701,10 +804,10 @@ hipError_t launch_layout(const GemmArgs &g, const Plan &p, hipStream_t stream)
 // K-contiguous A and B (A row-major, B column-major) on any tile; the
 // other three layouts on the tiles of the automatic choice (the 256 x 256
 // and 128 x 128 tiles), which the planner restricts them to.
-template <int T, int BM, int BN, int WM, int WN, int NS, int BK>
+template <int T, int BM, int BN, int WM, int WN, int NS, int BK, int MS = 32>
 hipError_t launch_one(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
-    return launch_layout<T, BM, BN, WM, WN, NS, BK, false, false>(g, p, stream);
+    return launch_layout<T, BM, BN, WM, WN, NS, BK, false, false, MS>(g, p, stream);
 }
 
 template <int T, int BM, int BN, int WM, int WN, int NS, int BK>
