@@ -150,13 +150,38 @@ __device__ __forceinline__ void store_chunk(const GemmArgs &g, const TileCoord &
     }
 }
 
-// LDS bytes tile_epilogue needs for a tile BN columns wide.  A staged row
-// is BN + 8 floats: the two 32-lane halves of a wave's accumulator write,
-// 4 rows apart, then fall on disjoint halves of the 64 banks, and rows stay
-// 16-byte aligned.
+// LDS bytes tile_epilogue needs for a tile BN columns wide, for
+// accumulators in MS x MS MFMA blocks.  A staged row is BN + 8 floats for
+// 32 x 32 blocks: the two 32-lane halves of a wave's accumulator write, 4
+// rows apart, then fall on disjoint halves of the 64 banks.  For 16 x 16
+// blocks it is BN + 20: the four 16-lane groups, 4 rows apart, fall on four
+// disjoint quarters.  Rows stay 16-byte aligned either way.
 constexpr int kEpilogueRows = 64;
-constexpr int epilogue_ld(int BN) { return BN + 8; }
-constexpr int epilogue_lds_bytes(int BN) { return (kEpilogueRows * epilogue_ld(BN) + BN) * 4; }
+constexpr int epilogue_ld(int BN, int MS = 32) { return MS == 32 ? BN + 8 : BN + 20; }
+constexpr int epilogue_lds_bytes(int BN, int MS = 32)
+{
+    return (kEpilogueRows * epilogue_ld(BN, MS) + BN) * 4;
+}
+
+// Block shape of an accumulator argument (a view type of 16 x 16 blocks
+// specialises it).
+template <typename ACC> struct acc_traits { static constexpr int MS = 32; };
+
+// A wave's FM x FN 16 x 16 accumulator blocks (v_mfma_f32_16x16x32_*), as
+// the epilogue takes them: it stages block (i, j) value v of lane 16 g + c
+// at row 16 i + 4 g + v, column 16 j + c of the wave tile.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+template <int FM, int FN>
+struct Acc16View {
+    const f32x4_t (&a)[FM][FN];
+};
+template <int FM, int FN> struct acc_traits<Acc16View<FM, FN>> { static constexpr int MS = 16; };
+
+template <int FM, int FN>
+__device__ __forceinline__ const f32x4_t &acc_block16(const Acc16View<FM, FN> &v, int i, int j)
+{
+    return v.a[i][j];
+}
 
 // The epilogue reads a wave's accumulators as FM x FN 32 x 32 blocks in the
 // 32 x 32 MFMA register layout, one block at a time through acc_block; a
@@ -179,7 +204,8 @@ __device__ __forceinline__ void stage_chunk(float *chunk, int c, const ACC &acc,
 {
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr int EP_ROWS = kEpilogueRows, EP_LD = epilogue_ld(BN);
+    constexpr int AMS = acc_traits<ACC>::MS;
+    constexpr int EP_ROWS = kEpilogueRows, EP_LD = epilogue_ld(BN, AMS);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int frag_half = lane >> 5;
@@ -187,15 +213,32 @@ __device__ __forceinline__ void stage_chunk(float *chunk, int c, const ACC &acc,
     for (int i = 0; i < FM; ++i) {
         const int row0 = wm * TM + i * 32 - c * EP_ROWS;   // block's first row in the chunk
         if (row0 >= 0 && row0 < EP_ROWS) {
+            if constexpr (AMS == 32) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const f32x16_t blk = acc_block(acc, i, j);
+                for (int j = 0; j < FN; ++j) {
+                    const f32x16_t &blk = acc_block(acc, i, j);
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = row0 + 8 * (v / 4) + 4 * frag_half + (v % 4);
-                    chunk[row * EP_LD + shift(c * EP_ROWS + row) + wn * TN + (lane & 31) + j * 32] =
-                        blk[v];
+                    for (int v = 0; v < 16; ++v) {
+                        const int row = row0 + 8 * (v / 4) + 4 * frag_half + (v % 4);
+                        chunk[row * EP_LD + shift(c * EP_ROWS + row) + wn * TN + (lane & 31) +
+                              j * 32] = blk[v];
+                    }
                 }
+            } else {
+                // 16 x 16 blocks 2i, 2i + 1: lane 16 g + c holds rows
+                // 4 g .. 4 g + 3 of column c
+#pragma unroll
+                for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                    for (int j = 0; j < 2 * FN; ++j) {
+                        const auto &blk = acc_block16(acc, 2 * i + bi, j);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int row = row0 + 16 * bi + 4 * (lane >> 4) + v;
+                            chunk[row * EP_LD + shift(c * EP_ROWS + row) + wn * TN + (lane & 15) +
+                                  j * 16] = blk[v];
+                        }
+                    }
             }
         }
     }
@@ -239,7 +282,8 @@ __device__ __forceinline__ void tile_epilogue_whole(const GemmArgs &g, char *out
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
     constexpr int CH_ROWS = 32 * WM;                  // tile rows per chunk
-    constexpr int EP_LD = epilogue_ld(BN);
+    constexpr int AMS = acc_traits<ACC>::MS;
+    constexpr int EP_LD = epilogue_ld(BN, AMS);
     constexpr bool HALF_OUT = OUT != DT_F32;
     constexpr int VEC = HALF_OUT ? 8 : 4;             // outputs per 16-byte block
     constexpr int ES = HALF_OUT ? 2 : 4;              // output element size
@@ -250,7 +294,7 @@ __device__ __forceinline__ void tile_epilogue_whole(const GemmArgs &g, char *out
     static_assert(CH_ROWS <= kEpilogueRows, "chunk fits the staging buffer");
     static_assert(NT % RPR == 0 && 32 % RSTEP == 0 && RUNS * RSTEP == CH_ROWS, "run split");
     static_assert(EDGE * NT == CH_ROWS * 2 * VEC, "edge split");
-    static_assert(epilogue_ld(BN) >= BN + VEC, "room for the row shift and the tail block");
+    static_assert(EP_LD >= BN + VEC, "room for the row shift and the tail block");
     // registers per run in flight (values, and C's when beta != 0); about
     // 40 more stay with addresses, bias and loop state
     constexpr int PER_RUN = VEC + (PARTIAL ? 0 : 4);
@@ -295,15 +339,32 @@ __device__ __forceinline__ void tile_epilogue_whole(const GemmArgs &g, char *out
     // Block row I of the wave's accumulators -> chunk rows wm * 32 + [0, 32),
     // each shifted by its tile row's misalignment.
     auto stage = [&](auto I) {
+        if constexpr (AMS == 32) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const f32x16_t blk = acc_block(acc, decltype(I)::value, j);
+            for (int j = 0; j < FN; ++j) {
+                const f32x16_t &blk = acc_block(acc, decltype(I)::value, j);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int rb = 8 * (v / 4) + 4 * frag_half + (v % 4);
-                lds[(wm * 32 + rb) * EP_LD + shift(wm * TM + decltype(I)::value * 32 + rb) +
-                    wn * TN + (lane & 31) + j * 32] = blk[v];
+                for (int v = 0; v < 16; ++v) {
+                    const int rb = 8 * (v / 4) + 4 * frag_half + (v % 4);
+                    lds[(wm * 32 + rb) * EP_LD + shift(wm * TM + decltype(I)::value * 32 + rb) +
+                        wn * TN + (lane & 31) + j * 32] = blk[v];
+                }
             }
+        } else {
+            // 16 x 16 blocks 2I, 2I + 1: lane 16 g + c holds rows 4 g .. 4 g + 3
+            // of column c
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int j = 0; j < 2 * FN; ++j) {
+                    const auto &blk = acc_block16(acc, 2 * decltype(I)::value + bi, j);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int rb = 16 * bi + 4 * (lane >> 4) + v;
+                        lds[(wm * 32 + rb) * EP_LD + shift(wm * TM + decltype(I)::value * 32 + rb) +
+                            wn * TN + (lane & 15) + j * 16] = blk[v];
+                    }
+                }
         }
     };
     // alpha, beta * C, bias and activation of one value at tile column col
@@ -473,13 +534,13 @@ __device__ __forceinline__ void tile_epilogue_rows(const GemmArgs &g, char *out,
                                                    const ACC &acc)
 {
     constexpr int NT = 64 * WM * WN;
-    constexpr int EP_ROWS = kEpilogueRows, EP_LD = epilogue_ld(BN);
+    constexpr int EP_ROWS = kEpilogueRows, EP_LD = epilogue_ld(BN, acc_traits<ACC>::MS);
     static_assert(!PARTIAL || OUT == DT_F32, "partials are fp32");
     constexpr bool HALF_OUT = OUT != DT_F32;
     constexpr int VEC = HALF_OUT ? 8 : 4;             // outputs per 16-byte run
     constexpr int RPR = BN / VEC + 1;                 // runs per row (head + full + tail)
     constexpr int ES = HALF_OUT ? 2 : 4;              // output element size
-    static_assert(epilogue_ld(BN) >= BN + VEC - 1, "room for the row shift");
+    static_assert(EP_LD >= BN + VEC - 1, "room for the row shift");
     const int tid = threadIdx.x;
     float *chunk = lds;
     float *bias_s = chunk + EP_ROWS * EP_LD;
@@ -623,7 +684,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs &g, const TileCoord
     }
     constexpr int NT = 64 * WM * WN;
     constexpr int EP_ROWS = kEpilogueRows;
-    constexpr int EP_LD = epilogue_ld(BN);
+    constexpr int EP_LD = epilogue_ld(BN, acc_traits<ACC>::MS);
     const int tid = threadIdx.x;
     float *chunk = lds;
     // the tile's BN bias values, read from global memory once

@@ -96,8 +96,6 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(f16x8_t a, f16x8_t b, f32x16_t
 // than the 32 x 32 x 16 shape on the same data (a probe of both shapes fed
 // from LDS: 1.64 against 1.45 PFLOP/s): half the accumulator register
 // traffic per flop.
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ f32x4_t mfma_16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -117,54 +115,6 @@ __device__ __forceinline__ f32x16_t mfma_block(F a, F b, f32x16_t c) { return mf
 template <typename F>
 __device__ __forceinline__ f32x4_t mfma_block(F a, F b, f32x4_t c) { return mfma_16x16x32(a, b, c); }
 
-// Four 16 x 16 accumulator blocks (rows 16 bi, columns 16 bj of a 32 x 32
-// block) rearranged into the 32 x 32 block's register layout (lane l,
-// value v: row 8 (v / 4) + 4 (l / 32) + v mod 4, column l mod 32), which the
-// epilogue reads.  Value v of lane 16 g + c in block (bi, bj) is row
-// 16 bi + 4 g + v, column 16 bj + c; it belongs in lane 32 (g mod 2) +
-// 16 bj + c, value 8 bi + 4 (g / 2) + v.  Per (bi, v) that is, in 16-lane
-// groups, [X0 X1 X2 X3], [Y0 Y1 Y2 Y3] (bj = 0, 1) -> [X0 Y0 X1 Y1],
-// [X2 Y2 X3 Y3]: a swap of odd groups of X with even groups of Y
-// (v_permlane16_swap), then of the upper half of the first result with
-// the lower half of the second (v_permlane32_swap), lane layouts measured
-// on gfx950.  Both instructions rewrite both of their registers; they are
-// written as assembly on two in-out operands because the compiler's
-// two-result builtins, chained, dropped the second result (both outputs
-// came back equal); not volatile, so that the compiler can place each
-// group's swaps next to the epilogue's use of it.  The s_nop keeps a VALU
-// write of either register two wait states away from the swap that reads
-// it.
-__device__ __forceinline__ f32x16_t acc16_to_32(const f32x4_t &b00, const f32x4_t &b01,
-                                                const f32x4_t &b10, const f32x4_t &b11)
-{
-    f32x16_t r;
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            float x = bi ? b10[v] : b00[v], y = bi ? b11[v] : b01[v];
-            asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\t"
-                "s_nop 1\n\tv_permlane32_swap_b32 %0, %1"
-                : "+v"(x), "+v"(y));
-            r[8 * bi + v] = x;
-            r[8 * bi + 4 + v] = y;
-        }
-    return r;
-}
-
-// A wave's FM x FN 16 x 16 accumulator blocks seen by the epilogue as
-// (FM / 2) x (FN / 2) 32 x 32 blocks.
-template <int FM, int FN>
-struct Acc16View {
-    const f32x4_t (&a)[FM][FN];
-};
-
-template <int FM, int FN>
-__device__ __forceinline__ f32x16_t acc_block(const Acc16View<FM, FN> &v, int i, int j)
-{
-    return acc16_to_32(v.a[2 * i][2 * j], v.a[2 * i][2 * j + 1], v.a[2 * i + 1][2 * j],
-                       v.a[2 * i + 1][2 * j + 1]);
-}
 
 
 // s_waitcnt immediate: wait until at most n vector-memory loads of this
@@ -271,11 +221,11 @@ __device__ __forceinline__ int swizzle_key(int r)
 
 // LDS of one workgroup: the stage ring, or the epilogue's chunk and bias
 // when those are larger (short rings of wide tiles).
-constexpr int mfma16_lds_bytes(int BM, int BN, int NS, int BK)
+constexpr int mfma16_lds_bytes(int BM, int BN, int NS, int BK, int MS = 32)
 {
-    return NS * (BM + BN) * (BK / 8) * 16 > epilogue_lds_bytes(BN)
+    return NS * (BM + BN) * (BK / 8) * 16 > epilogue_lds_bytes(BN, MS)
                ? NS * (BM + BN) * (BK / 8) * 16
-               : epilogue_lds_bytes(BN);
+               : epilogue_lds_bytes(BN, MS);
 }
 
 // Workgroups one CU holds at once: LDS allows 160 KB / mfma16_lds_bytes,
@@ -710,8 +660,6 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
         else
             tile_epilogue<BM, BN, WM, WN, REGS>(g, tc, (float *)lds, m0, n0, acc);
     } else {
-        // the epilogue reads 32 x 32 blocks, each rearranged from a 2 x 2
-        // group of 16 x 16 blocks where it is staged
         const Acc16View<FM, FN> view{acc};
         if (part)
             tile_epilogue_rows<BM, BN, WM, WN, true, DT_F32, REGS, false>(
@@ -788,7 +736,11 @@ void gemm_mfma_f16_kernel(GemmArgs g)
 template <int T, int BM, int BN, int WM, int WN, int NS, int BK, bool AT, bool BT, int MS = 32>
 hipError_t launch_layout(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
-    const size_t lds_bytes = (size_t)mfma16_lds_bytes(BM, BN, NS, BK);
+    const size_t lds_bytes = (size_t)mfma16_lds_bytes(BM, BN, NS, BK, MS);
+    static_assert(mfma16_per_cu(BM, BN, NS, BK) ==
+                      160 * 1024 / mfma16_lds_bytes(BM, BN, NS, BK, MS) ||
+                      mfma16_per_cu(BM, BN, NS, BK) < 160 * 1024 / mfma16_lds_bytes(BM, BN, NS, BK, MS),
+                  "the 16 x 16 epilogue's staging keeps the tile's occupancy");
     static_assert(64 * WM * WN == kSliverThreads, "sliver workgroups share the kernel's block");
     const int64_t programs = p.programs + g.sliver_blocks * g.sched.batch;
     const dim3 grid((unsigned)programs), block(64 * WM * WN);
