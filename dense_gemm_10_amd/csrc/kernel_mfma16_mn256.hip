@@ -8,10 +8,10 @@ hipError_t launch_mn256(const GemmArgs &g, const Plan &p, hipStream_t stream)
 {
     const bool at = g.a_col != 0, bt = g.b_col == 0;
     if (at && bt)
-        return launch_layout<T, 256, 256, 2, 2, 2, 64, true, true>(g, p, stream);
+        return launch_layout<T, 256, 256, 2, 2, 2, 64, true, true, 16>(g, p, stream);
     if (at)
-        return launch_layout<T, 256, 256, 2, 2, 2, 64, true, false>(g, p, stream);
-    return launch_layout<T, 256, 256, 2, 2, 2, 64, false, true>(g, p, stream);
+        return launch_layout<T, 256, 256, 2, 2, 2, 64, true, false, 16>(g, p, stream);
+    return launch_layout<T, 256, 256, 2, 2, 2, 64, false, true, 16>(g, p, stream);
 }
 
 hipError_t launch_mfma16_mn256(const GemmArgs &g, const Plan &p, hipStream_t stream)

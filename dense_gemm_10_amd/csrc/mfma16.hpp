@@ -246,10 +246,12 @@ constexpr int mfma16_per_cu(int BM, int BN, int NS, int BK)
 // Slot of logical 16-byte chunk c in k-row `k` of an operand staged with its
 // M (or N) dimension contiguous: rows sit 64 bytes apart modulo the 256
 // bytes of LDS banks, so the four k-rows one transposing read touches get
-// four disjoint quarters of the banks.
+// four disjoint quarters of the banks; k-rows 8 apart (the other 16-lane
+// group of the same half-wave in a 16 x 16 fragment read, or of the
+// second half-wave in a 32 x 32 one) take the other pair of chunks.
 __device__ __forceinline__ int mn_slot(int c, int k)
 {
-    return c ^ (4 * (k & 3));
+    return c ^ (4 * (k & 3)) ^ (2 * ((k >> 3) & 1));
 }
 
 // 8 16-bit elements at columns col .. col+7 of one row of an operand whose
@@ -328,8 +330,7 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
     constexpr int KS = MBK / KD;                 // MFMA k-steps per stage
     using acc_t = typename acc_of<MS>::type;
     constexpr int NV = MS == 32 ? 16 : 4;        // accumulators per lane per block
-    static_assert(MS == 32 || (MS == 16 && !AT && !BT),
-                  "16 x 16 blocks read K-contiguous operands only");
+    static_assert(MS == 32 || MS == 16, "MFMA block size");
     constexpr int RPI = 64 / CPR;                // stage rows per DMA instruction
     constexpr int ROWS = BM + BN;                // stage rows: A rows, then B columns
     constexpr int GROUPS = ROWS / RPI;           // DMA instructions per stage
@@ -515,22 +516,27 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
     // a k-step and columns 16 (g mod 2) + 4q .. + 3 of a fragment (see
     // tr_fragment).  Byte offset of that piece inside an M-/N-contiguous
     // part, k-step 0, first read, for the wave's fragment i (A) or j (B).
+    // With 16 x 16 blocks lane 16g + 4r + q addresses k-row 8g + r and
+    // columns 4q .. + 3 of the 16-column fragment, so lane 16g + i receives
+    // k-rows 8g .. 8g + 3 (and 8g + 4 .. 8g + 7 from the second read) of
+    // column i.
     const int tr_g = lane >> 4, tr_r = (lane >> 2) & 3, tr_q = lane & 3;
-    const int tr_krow = 8 * (tr_g >> 1) + tr_r;
-    const int tr_chunk = 2 * (tr_g & 1) + (tr_q >> 1);    // chunk inside a 32-column fragment
+    const int tr_krow = MS == 32 ? 8 * (tr_g >> 1) + tr_r : 8 * tr_g + tr_r;
+    // chunk inside the fragment's columns
+    const int tr_chunk = MS == 32 ? 2 * (tr_g & 1) + (tr_q >> 1) : tr_q >> 1;
     uint32_t a_tr[AT ? FM : 1], b_tr[BT ? FN : 1];
     if constexpr (AT) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             a_tr[i] = (uint32_t)(tr_krow * BM * 2 +
-                                 16 * mn_slot((wm * TM + 32 * i) / 8 + tr_chunk, tr_krow) +
+                                 16 * mn_slot((wm * TM + MS * i) / 8 + tr_chunk, tr_krow) +
                                  8 * (tr_q & 1));
     }
     if constexpr (BT) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             b_tr[j] = (uint32_t)(tr_krow * BN * 2 +
-                                 16 * mn_slot((wn * TN + 32 * j) / 8 + tr_chunk, tr_krow) +
+                                 16 * mn_slot((wn * TN + MS * j) / 8 + tr_chunk, tr_krow) +
                                  8 * (tr_q & 1));
     }
 
@@ -579,13 +585,13 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs &g, TileCoord tc, int
                 if (n < FM) {
                     if constexpr (AT)
                         fa[cur][n] = tr_fragment<frag_t, BM * 2>(a_addr + a_tr[n] +
-                                                                  16 * ks * BM * 2);
+                                                                  KD * ks * BM * 2);
                     else
                         fa[cur][n] = __builtin_bit_cast(frag_t, as[n * MS * CPR + c]);
                 } else if (n < FM + FN) {
                     if constexpr (BT)
                         fb[cur][n - FM] = tr_fragment<frag_t, BN * 2>(b_addr + b_tr[n - FM] +
-                                                                       16 * ks * BN * 2);
+                                                                       KD * ks * BN * 2);
                     else
                         fb[cur][n - FM] = __builtin_bit_cast(frag_t, bs[(n - FM) * MS * CPR + c]);
                 }
