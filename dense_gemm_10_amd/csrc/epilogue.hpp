@@ -1,5 +1,5 @@
 // Epilogue shared by the matrix-core kernels: a BM x BN tile of fp32
-// accumulators held in 32 x 32 MFMA blocks is staged through LDS in chunks
+// accumulators held in 32 x 32 (or 16 x 16) MFMA blocks is staged through LDS in chunks
 // of rows and stored along C's contiguous dimension in 16-byte runs, with
 // alpha, beta * C, bias and the activation applied once per element after
 // the K loop ("Skill: Write a Triton GEMM Kernel", Required reasoning
@@ -183,10 +183,10 @@ __device__ __forceinline__ const f32x4_t &acc_block16(const Acc16View<FM, FN> &v
     return v.a[i][j];
 }
 
-// The epilogue reads a wave's accumulators as FM x FN 32 x 32 blocks in the
-// 32 x 32 MFMA register layout, one block at a time through acc_block; a
-// kernel that accumulates in another layout passes a view type with its
-// own acc_block overload (found by argument-dependent lookup).
+// The epilogue reads a wave's accumulators one block at a time: FM x FN
+// 32 x 32 blocks in the 32 x 32 MFMA register layout through acc_block, or,
+// for an Acc16View (acc_traits MS = 16), 2FM x 2FN 16 x 16 blocks through
+// acc_block16, each staged in its own layout.
 template <int FM, int FN>
 __device__ __forceinline__ const f32x16_t &acc_block(const f32x16_t (&acc)[FM][FN], int i, int j)
 {
@@ -196,7 +196,8 @@ __device__ __forceinline__ const f32x16_t &acc_block(const f32x16_t (&acc)[FM][F
 // Accumulator blocks of rows [c * EP_ROWS, (c + 1) * EP_ROWS) of the tile into
 // the LDS chunk (fp32, row stride EP_LD).  Lane l's value v of a 32 x 32
 // block is row 8*(v/4) + 4*(l/32) + v%4, column l%32 of that block; wave
-// (wm, wn) owns blocks FM x FN at rows wm*TM + 32i, columns wn*TN + 32j.
+// (wm, wn) owns blocks FM x FN at rows wm*TM + 32i, columns wn*TN + 32j
+// (16 x 16 blocks: see Acc16View).
 // Tile row r is stored shifted right by shift(r) < 8 floats (0 for the
 // generic path), with EP_LD leaving room for it.
 template <int BM, int BN, int WM, int WN, typename Shift, typename ACC>

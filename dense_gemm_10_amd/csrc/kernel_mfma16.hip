@@ -7,9 +7,9 @@ namespace dg {
 // variant index -> instantiation (BM x BN tile, WM x WN wavefronts, ring
 // depth); the last field is mfma16_per_cu of the instantiation.
 // Entries 0 and 1 are the large and small tiles of the automatic choice:
-// 256 x 256 with whole-line (BK = 64) stages in a 2-stage ring, and
-// 128 x 128 with BK = 32 in a 4-stage ring (64 KB of LDS, two workgroups
-// per CU).  The others are selectable by name for sweeps.  The fp16 table
+// 256 x 256 with whole-line (BK = 64) stages in a 2-stage ring and 16 x 16
+// MFMA blocks, and 128 x 128 with BK = 32 in a 4-stage ring (64 KB of LDS,
+// two workgroups per CU).  The others are selectable by name for sweeps.  The fp16 table
 // has the same tiles.
 #define DG_TILE16(T, BM, BN, BK, NS, V) \
     {BM, BN, BK, 256, V, "mfma_" #T "_" #BM "x" #BN "x" #BK "_w2x2_s" #NS, mfma16_per_cu(BM, BN, NS, BK)}

@@ -1,4 +1,5 @@
-// Instantiations of the 16-bit matrix-core GEMM (mfma16.hpp): fp16, K-contiguous operands, tile variants 5 to 9.
+// Instantiations of the 16-bit matrix-core GEMM (mfma16.hpp): fp16, K-contiguous operands, tile variants 5 to 9
+// (variant 5, the 256 x 256 tile, on 16 x 16 x 32 MFMA blocks).
 #include "mfma16.hpp"
 
 namespace dg {

@@ -1,4 +1,5 @@
-// Instantiations of the 16-bit matrix-core GEMM (mfma16.hpp): an M- or N-contiguous operand, 256 x 256 tile, bf16 and fp16.
+// Instantiations of the 16-bit matrix-core GEMM (mfma16.hpp): an M- or N-contiguous operand, 256 x 256 tile
+// on 16 x 16 x 32 MFMA blocks, bf16 and fp16.
 #include "mfma16.hpp"
 
 namespace dg {

@@ -4,8 +4,8 @@
 // the dispatch.
 //
 // bf16 and fp16 GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16 and
-// its fp16 twin v_mfma_f32_32x32x16_f16; the 256 x 256 tile of K-contiguous
-// operands uses the 16 x 16 x 32 shapes, see mfma_16x16x32), fp32
+// its fp16 twin v_mfma_f32_32x32x16_f16; the 256 x 256 tile uses the
+// 16 x 16 x 32 shapes for every operand order, see mfma_16x16x32), fp32
 // accumulation.  The two element types share every byte of the data path
 // (loads, LDS layout, fragments, epilogue); only the MFMA instruction
 // differs.
