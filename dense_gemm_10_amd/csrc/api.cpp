@@ -662,6 +662,7 @@ void fill_args(const dg_gemm_desc *d, const Plan &p, const void *A, const void *
     g->sched.splits = p.splits;
     g->sched.group_m = d->group_m > 0 ? d->group_m : kDefaultGroupM;
     g->sched.xcd_remap = d->xcd_remap >= 0 ? 1 : 0;
+    sched_prepare(g->sched);
     g->sk = p.sk;
     g->sk_parts = p.sk.tail_tiles > 0 ? (float *)ws : nullptr;
 }
@@ -902,7 +903,13 @@ dg_status dg_schedule_map(int64_t M, int64_t N, int64_t batch, int32_t split_k, 
     a.splits = split_k;
     a.group_m = group_m > 0 ? group_m : kDefaultGroupM;
     a.xcd_remap = xcd_remap >= 0 ? 1 : 0;
-    const int64_t P = sched_programs(a);
+    // the decode's arithmetic is 32-bit: no launch has more programs
+    int64_t P;
+    if (__builtin_mul_overflow(a.num_pid_m, a.num_pid_n, &P) ||
+        __builtin_mul_overflow(P, a.batch, &P) || __builtin_mul_overflow(P, (int64_t)a.splits, &P) ||
+        P > INT32_MAX)
+        return DG_ERROR_NOT_SUPPORTED;
+    sched_prepare(a);
     if (P > 0 && (!out || out_len < 4 * P))
         return DG_ERROR_INVALID_VALUE;
     for (int64_t pid = 0; pid < P; ++pid) {

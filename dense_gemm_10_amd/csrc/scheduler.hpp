@@ -21,6 +21,13 @@
 //      band the tiles are taken column by column, top to bottom within a
 //      column.  A run of consecutive programs then reuses the same few A
 //      row panels and B column panels instead of sweeping a whole tile row.
+//
+// A launch has at most 2^31 - 1 programs, so the decode runs in 32-bit
+// unsigned arithmetic, and its divisions by the launch's counts (tiles per
+// matrix, tiles per band, band height, splits) are a multiply-high and two
+// shifts by constants the host prepares (sched_prepare): all scalar
+// instructions, where a division by a value known only at run time is a
+// chain of vector-to-scalar steps that delays a workgroup's first loads.
 #pragma once
 #include <stdint.h>
 
@@ -34,6 +41,23 @@ namespace dg {
 
 constexpr int kNumXcd = 8;
 
+// Division of any 32-bit n by an invariant d >= 1: with l = ceil(log2 d)
+// and m = floor(2^32 (2^l - d) / d) + 1 (which fits in 32 bits),
+// n / d = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0), t = mulhi(m, n)
+// (Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication", PLDI 1994, section 4, the unsigned case).
+// sh holds min(l, 1) in bit 8 and max(l - 1, 0) below it; d itself is
+// kept by the caller.
+struct FastDiv {
+    uint32_t m, sh;
+};
+
+DG_HD inline uint32_t fastdiv(uint32_t n, const FastDiv &f)
+{
+    const uint32_t t = (uint32_t)(((uint64_t)f.m * n) >> 32);
+    return (t + ((n - t) >> (f.sh >> 8))) >> (f.sh & 0xff);
+}
+
 struct SchedArgs {
     int64_t num_pid_m, num_pid_n;  // output tiles along M and N
     int64_t batch;
@@ -41,6 +65,12 @@ struct SchedArgs {
     int32_t group_m;               // >= 1
     int32_t xcd_remap;             // 1 = on
     int32_t pad_;
+    // filled by sched_prepare from the fields above: division by
+    FastDiv by_tiles;              // num_pid_m * num_pid_n
+    FastDiv by_band;               // group_m * num_pid_n, the tiles of a full band
+    FastDiv by_group;              // group_m, the rows of a full band
+    FastDiv by_last;               // the rows of the last band
+    FastDiv by_splits;             // splits
 };
 
 struct TileCoord {
@@ -55,6 +85,29 @@ DG_HD inline int64_t sched_programs(const SchedArgs &a)
     return a.batch * (int64_t)a.splits * a.num_pid_m * a.num_pid_n;
 }
 
+inline FastDiv fastdiv_make(uint32_t d)
+{
+    if (d == 0)
+        d = 1;     // a count of zero means an empty launch, which decodes nothing
+    uint32_t l = 0;
+    while (l < 32 && (1ull << l) < d)
+        ++l;
+    const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+    return FastDiv{(uint32_t)m, (l < 1 ? l : 1u) << 8 | (l > 1 ? l - 1 : 0u)};
+}
+
+// The divisors of a launch whose program count fits in 31 bits.
+inline void sched_prepare(SchedArgs &a)
+{
+    const int64_t G = a.group_m;
+    const int64_t bands = (a.num_pid_m + G - 1) / G;
+    a.by_tiles = fastdiv_make((uint32_t)(a.num_pid_m * a.num_pid_n));
+    a.by_band = fastdiv_make((uint32_t)(G * a.num_pid_n));
+    a.by_group = fastdiv_make((uint32_t)G);
+    a.by_last = fastdiv_make((uint32_t)(bands > 0 ? a.num_pid_m - (bands - 1) * G : 1));
+    a.by_splits = fastdiv_make((uint32_t)a.splits);
+}
+
 DG_HD inline int64_t xcd_remap(int64_t pid, int64_t P)
 {
     int64_t x = pid % kNumXcd;
@@ -66,32 +119,42 @@ DG_HD inline int64_t xcd_remap(int64_t pid, int64_t P)
 // (pid_m, pid_n); b and s are left 0.  Band `band` holds tile rows
 // [band * G, band * G + h) with h = min(G, rows left) and its h * num_pid_n
 // tiles; position o inside the band walks column o / h, row o mod h.
-DG_HD inline TileCoord decode_tile(int64_t t, const SchedArgs &a)
+DG_HD inline TileCoord decode_tile(int64_t t64, const SchedArgs &a)
 {
-    const int64_t G = a.group_m;
-    const int64_t band_tiles = G * a.num_pid_n;      // tiles of a full band
-    const int64_t band = t / band_tiles;
-    const int64_t o = t - band * band_tiles;         // position inside the band
-    const int64_t row0 = band * G;
-    const int64_t left = a.num_pid_m - row0;
-    const int64_t h = left < G ? left : G;           // rows in this band
+    const uint32_t t = (uint32_t)t64;
+    const uint32_t G = (uint32_t)a.group_m;
+    const uint32_t band = fastdiv(t, a.by_band);
+    const uint32_t o = t - band * (G * (uint32_t)a.num_pid_n);   // position inside the band
+    const uint32_t row0 = band * G;
+    // rows in this band: G, or what is left for the last band
+    const uint32_t left = (uint32_t)a.num_pid_m - row0;
+    const bool last = left < G;
+    const uint32_t h = last ? left : G;
+    const FastDiv fh{last ? a.by_last.m : a.by_group.m, last ? a.by_last.sh : a.by_group.sh};
+    const uint32_t col = fastdiv(o, fh);
     TileCoord c;
     c.b = 0;
     c.s = 0;
-    c.pid_m = (int32_t)(row0 + o % h);
-    c.pid_n = (int32_t)(o / h);
+    c.pid_m = (int32_t)(row0 + (o - col * h));
+    c.pid_n = (int32_t)col;
     return c;
 }
 
-DG_HD inline TileCoord decode_program(int64_t pid, const SchedArgs &a)
+DG_HD inline TileCoord decode_program(int64_t pid64, const SchedArgs &a)
 {
-    const int64_t T = a.num_pid_m * a.num_pid_n;
-    const int64_t P = a.batch * (int64_t)a.splits * T;
-    const int64_t L = a.xcd_remap ? xcd_remap(pid, P) : pid;
-    const int64_t bs = L / T;
-    TileCoord c = decode_tile(L % T, a);
-    c.s = (int32_t)(bs % a.splits);
-    c.b = bs / a.splits;
+    const uint32_t pid = (uint32_t)pid64;
+    const uint32_t T = (uint32_t)a.num_pid_m * (uint32_t)a.num_pid_n;
+    const uint32_t P = (uint32_t)a.batch * (uint32_t)a.splits * T;
+    uint32_t L = pid;
+    if (a.xcd_remap) {
+        const uint32_t x = pid % kNumXcd, q = P / kNumXcd, r = P % kNumXcd;
+        L = x * q + (x < r ? x : r) + pid / kNumXcd;
+    }
+    const uint32_t bs = fastdiv(L, a.by_tiles);
+    TileCoord c = decode_tile(L - bs * T, a);
+    const uint32_t b = fastdiv(bs, a.by_splits);
+    c.s = (int32_t)(bs - b * (uint32_t)a.splits);
+    c.b = b;
     return c;
 }
 
