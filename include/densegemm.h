@@ -259,7 +259,9 @@ dg_status dg_gemm_describe(const dg_gemm_desc *d, size_t workspace_bytes, char *
  * for every program id p < P = batch * S * ceil(M/bm) * ceil(N/bn) writes
  * out[4p .. 4p+3] = (batch index, split index, tile row, tile column) that
  * a kernel launched with that grid gives program p.  `out` is a HOST array
- * of 4*P int32.  Uses exactly the code the kernels use. */
+ * of 4*P int32.  Uses exactly the code the kernels use, which is 32-bit:
+ * P above 2^31 - 1 (more programs than any launch can have) returns
+ * DG_ERROR_NOT_SUPPORTED. */
 dg_status dg_schedule_map(int64_t M, int64_t N, int64_t batch, int32_t split_k, int32_t bm,
                           int32_t bn, int32_t group_m, int32_t xcd_remap, int32_t *out,
                           int64_t out_len);

@@ -109,6 +109,16 @@ def test_group_one_is_row_major():
     assert np.array_equal(m[:, 3], pid % 7)
 
 
+def test_grid_beyond_31_bits_is_refused():
+    # the decode is 32-bit: 2^31 - 1 programs pass the size check (and fail
+    # only for want of an output array), 2^31 and more are refused
+    lib = dg._load()
+    assert lib.dg_schedule_map(2**31 - 1, 1, 1, 1, 1, 1, 0, 0, None, 0) == dg.DG_ERROR_INVALID_VALUE
+    assert lib.dg_schedule_map(2**31, 1, 1, 1, 1, 1, 0, 0, None, 0) == dg.DG_ERROR_NOT_SUPPORTED
+    assert lib.dg_schedule_map(1 << 20, 1 << 20, 4, 1, 1, 1, 0, 0, None, 0) == dg.DG_ERROR_NOT_SUPPORTED
+    assert lib.dg_schedule_map(1 << 40, 1 << 40, 1 << 40, 8, 1, 1, 0, 0, None, 0) == dg.DG_ERROR_NOT_SUPPORTED
+
+
 def test_batch_and_split_decode_order():
     # without remap: tiles of one (b, s) are consecutive, then split, then batch
     m = dg.dg_schedule_map(2, 3, 4, 5, 1, 1, 8, -1)
