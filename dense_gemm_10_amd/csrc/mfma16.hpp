@@ -699,7 +699,8 @@ __device__ __forceinline__ void mfma16_program(const GemmArgs &g, uint4 *lds)
         // its XCD; an XCD's programs then share slices and tile rows.
         const int64_t n = sk.tail_tiles * sk.tail_splits;
         const int64_t i = g.sched.xcd_remap ? xcd_remap(pid - sk.dp_tiles, n) : pid - sk.dp_tiles;
-        const int64_t slice = i / sk.tail_tiles, r = i % sk.tail_tiles;
+        const uint32_t tt = (uint32_t)sk.tail_tiles;   // 32-bit, as the grid
+        const int64_t slice = (uint32_t)i / tt, r = (uint32_t)i % tt;
         tc = decode_tile(sk.dp_tiles + r, g.sched);
         kb = slice * sk.k_per_split;
         ke = kb + sk.k_per_split < g.K ? kb + sk.k_per_split : g.K;
@@ -717,8 +718,11 @@ __attribute__((amdgpu_waves_per_eu(mfma16_per_cu(BM, BN, kStages, MBK))))
 void gemm_mfma_bf16_kernel(GemmArgs g)
 {
     if (g.sliver_blocks && (int64_t)blockIdx.x >= g.main_programs) {
-        const int64_t i = (int64_t)blockIdx.x - g.main_programs;
-        sliver_block<DT_BF16, 1>(g, g.sliver_n0, 1, i % g.sliver_blocks, i / g.sliver_blocks);
+        // 32-bit (the grid is): a 64-bit division here costs the whole
+        // kernel scalar registers
+        const uint32_t i = blockIdx.x - (uint32_t)g.main_programs;
+        const uint32_t nb = (uint32_t)g.sliver_blocks;
+        sliver_block<DT_BF16, 1>(g, g.sliver_n0, 1, i % nb, i / nb);
         return;
     }
     extern __shared__ uint4 lds[];
@@ -731,8 +735,11 @@ __attribute__((amdgpu_waves_per_eu(mfma16_per_cu(BM, BN, kStages, MBK))))
 void gemm_mfma_f16_kernel(GemmArgs g)
 {
     if (g.sliver_blocks && (int64_t)blockIdx.x >= g.main_programs) {
-        const int64_t i = (int64_t)blockIdx.x - g.main_programs;
-        sliver_block<DT_F16, 1>(g, g.sliver_n0, 1, i % g.sliver_blocks, i / g.sliver_blocks);
+        // 32-bit (the grid is): a 64-bit division here costs the whole
+        // kernel scalar registers
+        const uint32_t i = blockIdx.x - (uint32_t)g.main_programs;
+        const uint32_t nb = (uint32_t)g.sliver_blocks;
+        sliver_block<DT_F16, 1>(g, g.sliver_n0, 1, i % nb, i / nb);
         return;
     }
     extern __shared__ uint4 lds[];
